@@ -1,0 +1,6 @@
+// Decode-step kernel instances for the gdn row of Table 1.
+#include "decode_impl.hpp"
+
+namespace rsq {
+DecodeFn decode_gdn(int cl, int feat) { return decode_pick_cl<kGDN>(cl, feat); }
+}  // namespace rsq

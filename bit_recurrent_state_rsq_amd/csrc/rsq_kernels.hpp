@@ -1,0 +1,110 @@
+// Kernel arguments and the pieces shared by the decode, readout and merge
+// kernels; host-side entry points to pick a kernel instance.
+#pragma once
+#include "rsq_device.hpp"
+
+namespace rsq {
+
+enum { kRetNet = 0, kMamba2 = 1, kGLA = 2, kGDN = 3 };
+enum { kScaleDynamic = 0, kScalePersistent = 1, kScaleYoked = 2 };
+// Compile-time feature variants of the decode kernel.
+enum { kFeatPlain = 0, kFeatBdr = 1, kFeatBypass = 2, kFeatYoked = 3, kFeatF32 = 4 };
+
+struct StepArgs {
+  uint8_t* tiles;            // state buffer + tiles offset
+  const HeadEntry* heads;    // head table (device)
+  uint32_t* status;          // device status word
+  int64_t* hdr_t;            // header step count
+  int32_t* hdr_n;            // header bypass fill
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  float* o;
+  uint64_t batch_stride;
+  int32_t H, dk, dv, group;
+  int32_t smode;
+  float trigger;
+  int32_t bdr;
+  float bdr_eps;
+  int32_t bypass;            // 1 when a low-rank bypass is configured
+  int32_t n;                 // bypass columns in use before this call
+  int32_t cap;               // k + m
+  int32_t lrb_k;
+  float lrb_eps;
+  int32_t in_bf16;           // q, k, v are bf16 (else fp32)
+  int32_t scale_f16;         // step sizes are stored as fp16 (else fp32)
+  int64_t t_next;
+};
+
+typedef void (*DecodeFn)(StepArgs);
+DecodeFn decode_kernel_for(int model, int cl, int feat);
+DecodeFn readout_kernel_for(int cl);
+DecodeFn merge_kernel_for(int cl);
+
+// Decay of key row i of a tile (Table 1, A_t column).
+__device__ __forceinline__ float row_decay(const StepArgs& a, const HeadEntry& he, int model,
+                                           int tile, int i) {
+  if (model == kRetNet) return he.gamma;
+  if (model == kGLA) return a.alpha[(size_t)tile * a.dk + i];
+  return a.alpha[tile];
+}
+
+__device__ __forceinline__ float in_elem(bool bf16, const void* p, size_t idx) {
+  if (bf16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[idx]);
+  return reinterpret_cast<const float*>(p)[idx];
+}
+
+// Bypass side of a decode step (Low-Rank Bypass of "Preserving Updates in
+// Low-Bit Recurrent State Quantization"; all of B_t goes to the bypass):
+//   U[:, c] <- RN16(a_i U_ic) for c < n, U[:, n] = fp16(k), W[:, n] = fp16(w),
+// and z_c = sum_i U_ic q_i (c <= n) for the readout term W z, left in lds_z.
+__device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
+                                    float* lds_z, int model) {
+  __half* U = reinterpret_cast<__half*>(tb + he.bypass_u);
+  __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
+  const int n = a.n;
+  float zacc[kMaxCap];
+#pragma unroll
+  for (int c = 0; c < kMaxCap; ++c) zacc[c] = 0.f;
+  for (int i = threadIdx.x; i < a.dk; i += blockDim.x) {
+    const float ai = row_decay(a, he, model, tile, i);
+    const float qi = in_elem(a.in_bf16, a.q, (size_t)tile * a.dk + i);
+    const float ki = in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i);
+#pragma unroll
+    for (int c = 0; c < kMaxCap; ++c) {
+      if (c < n) {
+        const __half un = mul_rn_half(ai, U[(size_t)c * a.dk + i]);
+        U[(size_t)c * a.dk + i] = un;
+        zacc[c] = __builtin_fmaf(__half2float(un), qi, zacc[c]);
+      } else if (c == n) {
+        const __half un = __float2half_rn(ki);
+        U[(size_t)c * a.dk + i] = un;
+        zacc[c] = __builtin_fmaf(__half2float(un), qi, zacc[c]);
+      }
+    }
+  }
+  for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
+    W[(size_t)n * a.dv + j] = __float2half_rn(in_elem(a.in_bf16, a.v, (size_t)tile * a.dv + j));
+  // block reduction of zacc[0..n]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  float* zpart = lds_z + kMaxCap;
+#pragma unroll
+  for (int c = 0; c < kMaxCap; ++c) {
+    if (c <= n) {
+      float v = zacc[c];
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == 0) zpart[wave * kMaxCap + c] = v;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x <= n) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += zpart[w * kMaxCap + threadIdx.x];
+    lds_z[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+}  // namespace rsq

@@ -32,7 +32,7 @@ the pairwise order of the Gated DeltaNet retrieval sum) is a reading, not
 something the pages fix; see each function. Where a function has no
 independent pin it says "parity unpinned".
 """
-from .fp import F32, F64, Arith, fma32, pairwise_sum, f16_round
+from .fp import F32, F64, Arith, fma32, pairwise_sum, f16_round, f16_of_exact
 from .recurrence import (OState, zero_state, step, merge, readout, decay_rows,
                          scale_rule, quantize_group_codes, qrange)
 from . import closed_form, brute, accounting

@@ -11,6 +11,7 @@ listed with each use). The pieces here are:
                      is a power of two: level 1 adds neighbours (x0+x1),
                      (x2+x3), ..., level 2 adds neighbouring pairs, and so on.
   f16_round          IEEE binary16 round-to-nearest-even (numpy's conversion)
+  f16_of_exact       the same from float64, for exact float32 x binary16 products
 
 Arith bundles the operations so that the recurrence is written once and run
 in 'f32' (canonical) or 'f64' (definitional) mode.
@@ -70,6 +71,12 @@ def f16_round(x):
     """IEEE binary16 round-to-nearest-even (overflow gives inf), as float32 values."""
     with np.errstate(over="ignore"):
         return np.asarray(x, dtype=f32).astype(np.float16).astype(f32)
+
+
+def f16_of_exact(x64):
+    """Round float64 values (exact products) once to binary16, nearest-even, as float32."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x64, dtype=np.float64).astype(np.float16).astype(f32)
 
 
 class Arith:

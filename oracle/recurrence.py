@@ -43,7 +43,8 @@ notes of the repository):
       |x - (c + sigma) s| stays within (0.5 + eps_B) s.
   R8  LRB: every update goes into the bypass as one fp16 column pair
       (U[:, n] = k, W[:, n] = w); between merges the quantized state only
-      decays, and U decays with it (U <- fp16(Diag(a) U)). A merge builds
+      decays, and U decays with it: U <- fp16(Diag(a) U), the exact product
+      rounded once to binary16. A merge builds
       L = U W^T, adds the elements with |L_ij| > eps_L * s_iG to the state,
       requantizes with BDR (sigma = sign(L_ij)), and keeps the best rank-k
       approximation of the rest as balanced fp16 factors; n becomes k.
@@ -60,7 +61,7 @@ from dataclasses import dataclass, field, replace
 from typing import Dict, Optional, Tuple
 import numpy as np
 
-from .fp import F32, F64, Arith, f16_round
+from .fp import F32, F64, Arith, f16_round, f16_of_exact
 
 FORGIVE = 1e-6   # decision-boundary window, in the units of each decision
 
@@ -348,7 +349,8 @@ def step(st: OState, inp: Dict, w, A: Arith = F32, static=None):
         if st.n >= cap:
             raise ValueError("bypass full: merge first")
         n = st.n
-        new.U[:, :, :n] = f16_round(A.mul(a[:, :, None], st.U[:, :, :n]))
+        # the exact product a_i U_ic (float32 x binary16 fits float64) rounded once to binary16
+        new.U[:, :, :n] = f16_of_exact(a[:, :, None].astype(np.float64) * st.U[:, :, :n].astype(np.float64))
         new.U[:, :, n] = f16_round(k)
         new.W[:, :, n] = f16_round(wv)
         new.n = n + 1

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP decode step against the CPU oracle, through the C ABI.
+
+Every test is teacher-forced (see harness.py): codes and step sizes bit-exact
+outside the 1e-6 decision windows, o_t and the dequantized state within
+rel-L2 1e-4 per step. The five workloads run at their full shapes; where the
+oracle cannot follow every tile at every step, a seeded sample of tiles that
+covers every head (and so every bit width) is checked at a spread of steps.
+"""
+import numpy as np
+import pytest
+
+from harness import (InputPool, Tally, compare, gpu_step, log, make_state, rel_l2, run_parity,
+                     sub_inputs, sub_static, sub_workload, tile_bits, to_device, to_oracle)
+import oracle
+from rsq_workloads import CONFIGS, static_params, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_tiles(w, per_head, seed=0):
+    rng = np.random.default_rng([seed, w.seed])
+    rows = rng.choice(w.batch, size=min(per_head, w.batch), replace=False)
+    return sorted(int(b) * w.heads + h for b in rows for h in range(w.heads))
+
+
+def test_cfg0_retnet_int4_every_step():
+    w = CONFIGS[0]
+    log("cfg0", w.name)
+    tally, st = run_parity(w, w.steps, check_steps=range(1, w.steps + 1))
+    tally.check()
+    assert st.counters() == (w.steps, 0)
+    assert st.get_status() == 0
+
+
+def test_cfg1_gdn_int4_persistent():
+    w = CONFIGS[1]
+    log("cfg1", w.name)
+    checks = list(range(1, 9)) + list(range(32, w.steps + 1, 64)) + [w.steps]
+    tiles = _sample_tiles(w, 4)
+    tally, st = run_parity(w, w.steps, check_steps=checks, tiles=tiles)
+    tally.check()
+    log("cfg1 forgiven", tally.forgiven, "of", tally.elements)
+
+
+def test_cfg1_gdn_all_tiles_first_steps():
+    w = CONFIGS[1]
+    tally, st = run_parity(w, 3, check_steps=[1, 2, 3])
+    tally.check()
+
+
+def test_cfg2_mamba2_int8_rows():
+    w = CONFIGS[2]
+    log("cfg2", w.name)
+    pool = InputPool.build(w, 16)
+    checks = [1, 2, 3, 100, 500, 1000, 1500, w.steps]
+    tally, st = run_parity(w, w.steps, check_steps=checks, tiles=_sample_tiles(w, 2), pool=pool)
+    tally.check()
+
+
+def test_cfg4_gdn_mixed_bits():
+    w = CONFIGS[4]
+    log("cfg4", w.name)
+    pool = InputPool.build(w, 8)
+    checks = [1, 2, 3, 64, 512, 1024, 2048, 3000, w.steps]
+    tally, st = run_parity(w, w.steps, check_steps=checks, tiles=_sample_tiles(w, 4), pool=pool)
+    tally.check()
+
+
+def test_cfg3_gla_bypass_decode_steps():
+    """Decode steps of the bypass workload up to the first merge point."""
+    w = CONFIGS[3]
+    tally, st = run_parity(w, w.lrb_k + w.lrb_m, check_steps=range(1, w.lrb_k + w.lrb_m + 1),
+                           tiles=_sample_tiles(w, 4), merge_check=lambda *a: None)
+    tally.check()
+    assert st.counters()[1] == w.lrb_k + w.lrb_m
+
+
+@pytest.mark.parametrize("model", ["retnet", "mamba2", "gla", "gdn"])
+def test_fp32_state_matches_oracle_bitwise(model):
+    base = {"retnet": CONFIGS[0], "gdn": CONFIGS[1], "mamba2": CONFIGS[2], "gla": CONFIGS[3]}[model]
+    w = base.with_(batch=3, heads=2, d_k=128, d_v=64, group=32, bits=32, mixed_bits=None,
+                   lrb_k=0, lrb_m=0, bdr=False, scale_mode="dynamic", seed=555)
+    tally, st = run_parity(w, 40, check_steps=range(1, 41))
+    assert tally.steps == 40
+
+
+@pytest.mark.parametrize("model,bits,g,mode,sdt", [
+    ("gdn", 8, 16, "dynamic", "f32"),
+    ("gdn", 6, 32, "persistent", "f16"),
+    ("mamba2", 4, 8, "persistent", "f32"),
+    ("retnet", 6, 64, "dynamic", "f16"),
+    ("gla", 8, 128, "dynamic", "f16"),
+    ("gla", 4, 32, "persistent", "f16"),
+])
+def test_small_variants(model, bits, g, mode, sdt):
+    base = {"retnet": CONFIGS[0], "gdn": CONFIGS[1], "mamba2": CONFIGS[2], "gla": CONFIGS[3]}[model]
+    dk = 128 if g <= 32 else (64 if g == 64 else 256)
+    dv = max(g, 32) * 2 if g < 128 else 128
+    w = base.with_(batch=2, heads=3, d_k=dk, d_v=dv, group=g, bits=bits, mixed_bits=None,
+                   scale_mode=mode, scale_dtype=sdt, lrb_k=0, lrb_m=0, bdr=False, seed=777 + bits)
+    tally, st = run_parity(w, 24, check_steps=range(1, 25))
+    tally.check()
+
+
+@pytest.mark.parametrize("model", ["gdn", "gla"])
+def test_bdr_without_bypass(model):
+    base = CONFIGS[1] if model == "gdn" else CONFIGS[3]
+    w = base.with_(batch=2, heads=4, d_k=128, d_v=64, group=32, bits=4, bdr=True, bdr_eps=0.3,
+                   lrb_k=0, lrb_m=0, scale_mode="dynamic", scale_dtype="f16", seed=991)
+    tally, st = run_parity(w, 32, check_steps=range(1, 33))
+    tally.check()
+
+
+@pytest.mark.parametrize("model", ["gdn", "mamba2"])
+def test_yoked_scales(model):
+    base = CONFIGS[1] if model == "gdn" else CONFIGS[2]
+    w = base.with_(batch=2, heads=2, d_k=128, d_v=64, group=32, bits=4, scale_mode="yoked",
+                   scale_dtype="f16", lrb_k=0, lrb_m=0, seed=4321, bdr=(model == "gdn"))
+    tally, st = run_parity(w, 40, check_steps=range(1, 41))
+    tally.check()
+    from bit_recurrent_state_rsq_amd import _abi
+    assert st.get_status() & _abi.F_CLIPPED      # the scale follows the reference, codes clip
+
+
+def test_gdn_with_d_k_256_crosses_wavefronts():
+    w = CONFIGS[1].with_(batch=2, heads=2, d_k=256, d_v=64, seed=31)
+    tally, st = run_parity(w, 16, check_steps=range(1, 17))
+    tally.check()
+
+
+def test_readout_call_matches_dequantized_state():
+    import torch
+    w = CONFIGS[4].with_(batch=4)
+    tally, st = run_parity(w, 10, check_steps=[10], tiles=list(range(w.tiles)))
+    arrs = st.read_tiles()
+    inp = step_inputs(w, 11, static_params(w))
+    dev = to_device(inp, w)
+    o = st.readout(dev["q"]).reshape(w.tiles, -1).cpu().numpy()
+    ost = to_oracle(arrs, w, list(range(w.tiles)), 0)
+    o_ref = oracle.readout(ost, inp["q"], w)
+    assert rel_l2(o, o_ref) <= 1e-5
+
+
+def test_nonfinite_input_sets_the_status_flag():
+    import torch
+    from bit_recurrent_state_rsq_amd import _abi
+    w = CONFIGS[1].with_(batch=1, heads=2)
+    st = make_state(w)
+    inp = step_inputs(w, 1, static_params(w))
+    dev = to_device(inp, w)
+    gpu_step(st, dev)
+    assert st.get_status() == 0
+    dev["v"][0, 1, 3] = float("inf")
+    gpu_step(st, dev)
+    assert st.get_status() & _abi.F_NONFINITE
+    assert st.get_status() == 0          # reading clears the word
+
+
+def test_attach_restores_a_saved_state():
+    import torch
+    import bit_recurrent_state_rsq_amd as rsq
+    w = CONFIGS[4].with_(batch=2)
+    st = make_state(w)
+    static = static_params(w)
+    for t in range(1, 6):
+        gpu_step(st, to_device(step_inputs(w, t, static), w))
+    saved = st.buf.clone()
+    kw = dict(st.kw)
+    st2 = rsq.State(buffer=saved, attach=True, **kw)
+    assert st2.counters() == (5, 0)
+    d6 = to_device(step_inputs(w, 6, static), w)
+    o1 = gpu_step(st, d6)
+    o2 = gpu_step(st2, d6)
+    assert torch.equal(o1, o2)
+    assert torch.equal(st.buf, saved)
+    # a different configuration does not attach
+    with pytest.raises(rsq.Error) as e:
+        rsq.State(buffer=saved, attach=True, **dict(kw, group=16))
+    assert e.value.code in (rsq._abi.RSQ_E_ATTACH, rsq._abi.RSQ_E_BUFFER)
+
+
+def test_full_bypass_refuses_a_decode_step():
+    import bit_recurrent_state_rsq_amd as rsq
+    w = CONFIGS[3].with_(batch=1, heads=2, lrb_k=1, lrb_m=2)
+    st = make_state(w)
+    static = static_params(w)
+    for t in range(1, 4):
+        gpu_step(st, to_device(step_inputs(w, t, static), w))
+    with pytest.raises(rsq.Error) as e:
+        gpu_step(st, to_device(step_inputs(w, 4, static), w))
+    assert e.value.code == rsq._abi.RSQ_E_BYPASS_FULL

@@ -3,7 +3,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle.fp import fma32, pairwise_sum, f16_round, F32
+from oracle.fp import fma32, pairwise_sum, f16_round, f16_of_exact, F32
 
 
 def _rn32(q: Fraction) -> np.float32:
@@ -90,3 +90,38 @@ def test_f16_round_ties_and_subnormals():
                     np.float32)
     exp = np.array([1.0, 1 + 2 ** -9, 2 ** -24, 0.0, 2 ** -23, 65504.0, np.inf], np.float32)
     assert np.array_equal(f16_round(vals), exp)
+
+
+def _rn16(q: Fraction) -> float:
+    """Correctly rounded binary16 of an exact rational (ties to even), by bracketing."""
+    if q == 0:
+        return 0.0
+    h = np.float16(float(q))
+    cands = [np.nextafter(h, np.float16(-np.inf)), h, np.nextafter(h, np.float16(np.inf))]
+    best = None
+    for c in cands:
+        if not np.isfinite(c):
+            continue
+        d = abs(Fraction(float(c)) - q)
+        if best is None or d < best[0] or (d == best[0] and (int(np.float16(c).view(np.uint16)) & 1) == 0):
+            best = (d, c)
+    return float(best[1])
+
+
+def test_f16_of_exact_rounds_products_once():
+    rng = np.random.default_rng(21)
+    a = rng.uniform(0.5, 1.0, 4000).astype(np.float32)
+    u = (rng.standard_normal(4000) * np.exp2(rng.integers(-26, 4, 4000))).astype(np.float16)
+    got = f16_of_exact(a.astype(np.float64) * u.astype(np.float64))
+    for i in range(len(a)):
+        exact = Fraction(float(a[i])) * Fraction(float(u[i]))
+        assert float(got[i]) == _rn16(exact), (a[i], u[i])
+    # the single rounding differs from rounding to float32 first on some inputs
+    a = rng.uniform(0.5, 1.0, 2_000_000).astype(np.float32)
+    u = rng.standard_normal(2_000_000).astype(np.float16)
+    once = f16_of_exact(a.astype(np.float64) * u.astype(np.float64))
+    twice = f16_round((a * u.astype(np.float32)).astype(np.float32))
+    i = np.flatnonzero(once != twice)
+    assert len(i) > 0
+    exact = Fraction(float(a[i[0]])) * Fraction(float(u[i[0]]))
+    assert float(once[i[0]]) == _rn16(exact)
