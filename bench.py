@@ -93,7 +93,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before timing (default: 24 per rotated state set, at least 64)")
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--warm", action="store_true", help="time one state set in place (cache-warm)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -140,6 +141,8 @@ def main():
         if cap and st.counters()[1] == cap:
             st.merge_bypass()
 
+    if args.warmup is None:
+        args.warmup = max(64, 24 * nsets)
     for s in range(args.warmup):
         one_step(s, states[s % nsets])
     torch.cuda.synchronize()

@@ -2,5 +2,5 @@
 #include "decode_impl.hpp"
 
 namespace rsq {
-DecodeFn decode_gla(int cl, int feat) { return decode_pick_cl<kGLA>(cl, feat); }
+DecodeFn decode_gla(int cl, int feat, int spec) { return decode_pick_cl<kGLA>(cl, feat, spec); }
 }  // namespace rsq

@@ -21,21 +21,175 @@
 // Table 1 and the update/requantize/BDR/LRB definitions are from "Preserving
 // Updates in Low-Bit Recurrent State Quantization"; the scale policies from
 // the abstract of "When Dynamic Scaling Fails ...".
+//
+// Instruction diet (the step moves ~1.2 bytes per element, so at HBM speed a
+// lane has only a handful of VALU slots per element):
+//  * codes are unpacked straight to F*c with one SDWA sign-extending convert
+//    per code (F = 16, 4, 1 for 4, 6, 8 bits); 1/F is folded into the per-row
+//    multipliers, which is exact whenever the multiplier is not deep in the
+//    float32 subnormal range (checked; the exact long form runs otherwise);
+//  * with bf16 keys and binary16 step sizes, k_i s_i and c k_i s_i are exact in
+//    float32 (19 and <= 24 bits), so the first cascade level of the retrieval
+//    is one FMA per pair of rows;
+//  * row sums use permlane swaps / DPP, halving the carried columns per level;
+//  * 1/s for a binary16 step is rcp + one Newton step, which reproduces the
+//    correctly rounded reciprocal for every binary16 value (checked on the
+//    device for all 31743 positive finite values);
+//  * requantization is one FMA against 1.5*2^23 + 2^(b-1): the float's low bits
+//    are then the offset-binary code; the clamp runs only when a step size is
+//    small enough (a subnormal, or a yoked scale) for a code to leave the range.
 #pragma once
 #include "rsq_kernels.hpp"
+#include "lane_ops.hpp"
 
 namespace rsq {
 
-template <int MODEL, int CL, int FEAT>
+template <int BITS>
+struct Fmt {
+  static constexpr float F = BITS == 4 ? 16.f : BITS == 6 ? 4.f : 1.f;   // unpacked value = F * code
+  static constexpr float invF = 1.f / F;
+  static constexpr int qmax = (1 << (BITS - 1)) - 1;
+  static constexpr float magic = 12582912.0f + (float)(1 << (BITS - 1));  // 1.5*2^23 + 2^(b-1)
+  // products c * (k s) stay exact in float32 (|c| < 2^(b-1), k s has 19 bits)
+  static constexpr bool kExactPairs = BITS <= 6;
+};
+
+// ---------------------------------------------------------------- unpack to F*c
+__device__ __forceinline__ void unpack_scaled(const Chunk<4>& ch, float c[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t lo = (ch.w[r] << 4) & 0xF0F0F0F0u;
+    const uint32_t hi = ch.w[r] & 0xF0F0F0F0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      c[r][b] = (float)(int8_t)(lo >> (8 * b));
+      c[r][b + 4] = (float)(int8_t)(hi >> (8 * b));
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack_scaled(const Chunk<8>& ch, float c[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      c[r][b] = (float)(int8_t)(ch.w[2 * r] >> (8 * b));
+      c[r][b + 4] = (float)(int8_t)(ch.w[2 * r + 1] >> (8 * b));
+    }
+}
+
+// bytes hi<<4 | lo<<2 sign-extend to 16 hi + 4 lo = 4 c
+__device__ __forceinline__ void unpack_scaled(const Chunk<6>& ch, float c[8][8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t cw = ch.w[8 + (r >> 1)] >> ((r & 1) * 4);
+    const uint32_t lo = ((ch.w[r] << 4) & 0xF0F0F0F0u) | ((cw << 2) & 0x0C0C0C0Cu);
+    const uint32_t hi = (ch.w[r] & 0xF0F0F0F0u) | (cw & 0x0C0C0C0Cu);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      c[r][b] = (float)(int8_t)(lo >> (8 * b));
+      c[r][b + 4] = (float)(int8_t)(hi >> (8 * b));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pack offset codes
+// t holds 1.5*2^23 + 2^(b-1) + c; its low byte is the offset-binary code.
+__device__ __forceinline__ uint32_t gather_low_bytes(float a, float b, float c, float d) {
+  const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0c0c0400u);
+  return ab | (cd << 16);
+}
+
+__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<4>& ch) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const uint32_t lo = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
+    const uint32_t hi = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
+    ch.w[r] = (lo | (hi << 4)) ^ 0x88888888u;     // offset binary -> two's complement nibbles
+  }
+}
+
+__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<8>& ch) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    ch.w[2 * r] = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]) ^ 0x80808080u;
+    ch.w[2 * r + 1] = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]) ^ 0x80808080u;
+  }
+}
+
+__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<6>& ch) {
+  uint32_t L[8], H[8];   // offset codes u = c + 32, one per byte
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    L[r] = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
+    H[r] = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
+    // high nibble of the two's complement code: (u >> 2) ^ 8
+    ch.w[r] = (((L[r] >> 2) & 0x0F0F0F0Fu) | ((H[r] << 2) & 0xF0F0F0F0u)) ^ 0x88888888u;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t m = 0x03030303u;
+    ch.w[8 + p] = (L[2 * p] & m) | ((H[2 * p] & m) << 2) | ((L[2 * p + 1] & m) << 4) | ((H[2 * p + 1] & m) << 6);
+  }
+}
+
+// correctly rounded 1/s of a binary16 value (s > 0 finite), see the header note
+__device__ __forceinline__ float recip_f16val(float s) {
+  const float r = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, r, 1.0f);
+  return __builtin_fmaf(r, e, r);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+__device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
+
+// m / F (F a small power of two) is exact unless the quotient is subnormal
+__device__ __forceinline__ bool subnormal(float m) { return __builtin_amdgcn_class(m, 0x90) != 0; }
+
+// Compile-time specialisations of the per-call flags (0 = read them at run time):
+// scale mode, step-size dtype, input dtype and scale group size.
+enum { kSpecGeneric = 0, kSpecPersF16Bf16G32 = 1, kSpecDynF32Bf16G64 = 2, kSpecDynF16Bf16G32 = 3,
+       kSpecDynF32F32G64 = 4 };
+enum { kSpecPersF16Bf16 = kSpecPersF16Bf16G32, kSpecDynF32Bf16 = kSpecDynF32Bf16G64,
+       kSpecDynF16Bf16 = kSpecDynF16Bf16G32, kSpecDynF32F32 = kSpecDynF32F32G64 };
+
+template <int SPEC>
+struct Spec {
+  // lanes per scale group (0: run time)
+  static constexpr int GL = SPEC == kSpecGeneric ? 0 : (SPEC == 1 || SPEC == 3) ? 4 : 8;
+  static __device__ __forceinline__ int smode(const StepArgs& a) {
+    return SPEC == kSpecGeneric ? a.smode : SPEC == kSpecPersF16Bf16 ? (int)kScalePersistent : (int)kScaleDynamic;
+  }
+  static __device__ __forceinline__ bool sf16(const StepArgs& a) {
+    return SPEC == kSpecGeneric ? a.scale_f16 != 0 : (SPEC == kSpecPersF16Bf16 || SPEC == kSpecDynF16Bf16);
+  }
+  static __device__ __forceinline__ bool bf16(const StepArgs& a) {
+    return SPEC == kSpecGeneric ? a.in_bf16 != 0 : SPEC != kSpecDynF32F32;
+  }
+};
+
+template <int MODEL, int CL, int FEAT, int SPEC>
 struct Decode {
+  using SP = Spec<SPEC>;
   static constexpr int RL = 64 / CL;
   static constexpr int NB = (RL == 16) ? 4 : (RL == 8) ? 3 : 2;   // log2(RL)
   static constexpr int WR = 8 * RL;
   static constexpr int WC = 8 * CL;
+  static constexpr int NSLOT = 8 >> (NB < 3 ? NB : 3);            // columns a lane holds after xtree
+  static constexpr bool kF32 = FEAT == kFeatF32;
+  static constexpr bool kBypass = FEAT == kFeatBypass;
+  static constexpr bool kYoked = FEAT == kFeatYoked;
 
-  // Row decays of the lane's 8 rows.
-  static __device__ __forceinline__ void decays(const StepArgs& a, const HeadEntry& he, int tile,
-                                                int i0, float dec[8]) {
+  struct Lds {
+    float* w;      // [nwaves][WC]   per-wavefront broadcast of w (and of the reference's w)
+    float* up;     // [wrw][dv]      retrieval partials across row-wavefronts
+    float* op;     // [wrw][dv]      readout partials across row-wavefronts
+    float* z;      // [kMaxCap] + [nwaves][kMaxCap]  bypass readout projections
+  };
+
+  static __device__ __forceinline__ void decays(const StepArgs& a, const HeadEntry& he, int tile, int i0,
+                                                float dec[8]) {
     if constexpr (MODEL == kRetNet) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) dec[r] = he.gamma;
@@ -48,44 +202,101 @@ struct Decode {
     }
   }
 
-  // Cascade sum of one lane value per column over the wavefront's row blocks,
-  // in row-block order (lane bit 5 holds the lowest row-block bit).
-  static __device__ __forceinline__ float rows_tree(float p) {
+  // Finish a per-column row sum (v: NSLOT wave sums of this lane's columns)
+  // across row-wavefronts in cascade order; every wave of the column stripe
+  // ends with the full sum. The caller passes the LDS partial buffer.
+  static __device__ __forceinline__ void across_waves(float v[8], float* part, int wrw, int wr, int j0,
+                                                      int lane, int dv) {
+    if (wrw <= 1) return;
+    const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
 #pragma unroll
-    for (int s = 0; s < NB; ++s) p = __fadd_rn(p, shfl_xor(p, 32 >> s));
-    return p;
+    for (int s = 0; s < NSLOT; ++s)
+      if (writer) part[wr * dv + j0 + xtree_col<NB>(s, lane)] = v[s];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const int col = j0 + xtree_col<NB>(s, lane);
+      float l0 = part[col], l1 = part[dv + col];
+      if (wrw == 2) {
+        v[s] = __fadd_rn(l0, l1);
+      } else {
+        const float l2 = part[2 * dv + col], l3 = part[3 * dv + col];
+        float a01 = __fadd_rn(l0, l1), a23 = __fadd_rn(l2, l3);
+        if (wrw == 4) {
+          v[s] = __fadd_rn(a01, a23);
+        } else {
+          const float b01 = __fadd_rn(__fadd_rn(part[4 * dv + col], part[5 * dv + col]),
+                                      __fadd_rn(part[6 * dv + col], part[7 * dv + col]));
+          v[s] = __fadd_rn(__fadd_rn(a01, a23), b01);
+        }
+      }
+    }
+    __syncthreads();
   }
 
-  // Finish u_j across row-wavefronts (the top levels of the cascade).
-  static __device__ __forceinline__ void rows_tree_waves(float u[8], float* upart, int wrw, int wr, int lr,
-                                                         int j0, int dv) {
-    if (wrw > 1) {
-      if (lr == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) upart[wr * dv + j0 + j] = u[j];
-      }
-      __syncthreads();
+  // u_j = sum_i k_i S_ij in cascade order for the lane's 8 columns, turned into
+  // w_j = beta (v_j - alpha u_j), broadcast to every lane of the column block.
+  // xs: the lane's 8x8 values with S_ij = xs_ij * mul_i (mul = s/F, or 1 for an
+  // fp32 tile); kap: k_i s_i / F when `fast` (exact products), unused otherwise.
+  template <int BITS>
+  static __device__ __forceinline__ void delta_w(const StepArgs& a, int tile, const float xs[8][8],
+                                                 const float kf[8], const float mul[8], const float kap[8],
+                                                 bool fast, float wv[8], float* wl,
+                                                 float* up, int wrw, int wr, int j0, int lane, int wave) {
+    float v8[8];
+    if (fast) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float lvl[8];
-        for (int q = 0; q < wrw; ++q) lvl[q] = upart[q * dv + j0 + j];
-        for (int n = wrw; n > 1; n >>= 1)
-          for (int q = 0; q < n / 2; ++q) lvl[q] = __fadd_rn(lvl[2 * q], lvl[2 * q + 1]);
-        u[j] = lvl[0];
+        float p[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float t0 = __fmul_rn(xs[2 * q][j], kap[2 * q]);
+          if constexpr (Fmt<BITS>::kExactPairs) {
+            p[q] = __builtin_fmaf(xs[2 * q + 1][j], kap[2 * q + 1], t0);   // = fl(t0 + t1), t1 exact
+          } else {
+            p[q] = __fadd_rn(t0, __fmul_rn(xs[2 * q + 1][j], kap[2 * q + 1]));
+          }
+        }
+        v8[j] = __fadd_rn(__fadd_rn(p[0], p[1]), __fadd_rn(p[2], p[3]));
       }
-      __syncthreads();
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(kf[i], __fmul_rn(xs[i][j], mul[i]));
+        v8[j] = tree8(t);
+      }
     }
+    xtree<NB>(v8, lane);
+    across_waves(v8, up, wrw, wr, j0, lane, a.dv);
+    const float al = a.alpha[tile], be = a.beta[tile];
+    // lanes holding column sums compute w and publish it
+    float* wrow = wl + wave * WC;
+    const int lc = lane % CL;
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const int c = xtree_col<NB>(s, lane);
+      const float vj = load_in1(a, tile, j0 + c);
+      const float w = __fmul_rn(be, __fsub_rn(vj, __fmul_rn(al, v8[s])));
+      if (NB < 4 || ((lane >> 2) & 1) == 0) wrow[8 * lc + c] = w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    loadf8(wrow + 8 * lc, wv);
+  }
+
+  static __device__ __forceinline__ float load_in1(const StepArgs& a, int tile, int j) {
+    return in_elem(SP::bf16(a), a.v, (size_t)tile * a.dv + j);
   }
 
   template <int BITS>
   static __device__ __forceinline__ void body(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                              float* lds_o, float* lds_u, float* lds_ur, uint32_t& flags) {
-    constexpr bool kF32 = FEAT == kFeatF32;
-    constexpr bool kBypass = FEAT == kFeatBypass;
-    constexpr bool kYoked = FEAT == kFeatYoked;
-    const bool bdr = (FEAT == kFeatBdr) || (kYoked && a.bdr);
-    const bool bf16 = a.in_bf16 != 0, sf16 = a.scale_f16 != 0;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                              const Lds& L, uint32_t& flags) {
+    const bool bf16 = SP::bf16(a), sf16 = SP::sf16(a);
+    const int smode = SP::smode(a);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int wrw = a.dk / WR;
     const int wr = wave % wrw, wc = wave / wrw;
     const int lc = lane % CL, lr = lane / CL;
@@ -94,81 +305,97 @@ struct Decode {
     const int j0 = wc * WC + 8 * lc;
     const int G = j0 / a.group;
     const int gl = a.group >> 3;        // lanes per group (1..16)
-
-    float qf[8], kf[8], vf[8], dec[8];
-    load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
-    load8(bf16, a.k, (size_t)tile * a.dk + i0, kf);
-    load8(bf16, a.v, (size_t)tile * a.dv + j0, vf);
-    decays(a, he, tile, i0, dec);
+    constexpr float F = kF32 ? 1.f : Fmt<BITS == 32 ? 8 : BITS>::F;
+    constexpr float invF = 1.f / F;
 
     uint8_t* cp = tb + ((size_t)(j0 >> 3) * (a.dk >> 3) + (i0 >> 3)) * (8 * BITS);
     uint8_t* sp = tb + he.scales + ((size_t)G * a.dk + i0) * (sf16 ? 2 : 4);
-    // x starts as the codes (or the fp32 state) and becomes the updated state
     float x[8][8];
     float s_old[8];
     if constexpr (kF32) {
       load_f32_chunk(cp, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s_old[i] = 1.f;
     } else {
       Chunk<BITS> ch;
       load_chunk<BITS>(cp, ch);
       load_scales8(sf16, sp, s_old);
-      unpack(ch, x);
+      unpack_scaled(ch, x);
     }
+    float qf[8], kf[8], dec[8];
+    load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
+    load8(bf16, a.k, (size_t)tile * a.dk + i0, kf);
+    decays(a, he, tile, i0, dec);
 
-    // delta rule: w = beta (v - alpha S^T k), S^T k as a cascade sum over rows
-    float wv[8];
-    if constexpr (MODEL == kGDN) {
-      const float al = a.alpha[tile], be = a.beta[tile];
-      float u[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(kf[i], kF32 ? x[i][j] : __fmul_rn(x[i][j], s_old[i]));
-        u[j] = rows_tree(tree8(t));
-      }
-      rows_tree_waves(u, lds_u, wrw, wr, lr, j0, a.dv);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = __fmul_rn(be, __fsub_rn(vf[j], __fmul_rn(al, u[j])));
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = vf[j];
-    }
-
-    // decay, then the update: x = fma(k_i, w_j, r_ij), r_ij = fl(c_ij fl(a_i s_i))
-    float r[kBypass ? 1 : 8][8];   // kept for BDR only
+    // per-row multipliers: c1/F (decay) and k s / F (retrieval)
+    float c1p[8], kap[8], smul[8];
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float c1 = kF32 ? dec[i] : __fmul_rn(dec[i], s_old[i]);
+      c1p[i] = __fmul_rn(c1, invF);
+      if constexpr (!kF32) bad = bad || subnormal(c1p[i]);
+      smul[i] = kF32 ? 1.f : s_old[i];
+      if constexpr (MODEL == kGDN && !kF32) {
+        kap[i] = __fmul_rn(__fmul_rn(kf[i], s_old[i]), invF);
+        bad = bad || subnormal(kap[i]);
+      }
+    }
+    const bool fast = !wave_any(bad) && (kF32 || MODEL != kGDN || (bf16 && sf16));
+    if (!fast) {
+      // exact long form: bring x back to the codes themselves
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ri = __fmul_rn(x[i][j], c1);
-        if constexpr (!kBypass) {
-          r[i][j] = ri;
-          x[i][j] = __builtin_fmaf(kf[i], wv[j], ri);
-        } else {
-          x[i][j] = ri;
-        }
+      for (int i = 0; i < 8; ++i) {
+        c1p[i] = kF32 ? dec[i] : __fmul_rn(dec[i], s_old[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(x[i][j], invF);
       }
     }
 
-    // readout partial o_j = sum_i q_i x_ij over this wavefront's rows
+    // update B_t: w = v, or the delta rule
+    float wv[8];
+    if constexpr (MODEL == kGDN) {
+      delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kF32, wv, L.w, L.up, wrw, wr, j0,
+                                     lane, wave);
+    } else {
+      load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
+    }
+
+    // decay and update; r = fl(c fl(a s)) kept for BDR
+    constexpr bool kKeepR = !kBypass && !kF32;
+    float r[kKeepR ? 8 : 1][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ri = __fmul_rn(x[i][j], c1p[i]);
+        if constexpr (kKeepR) r[i][j] = ri;
+        if constexpr (kBypass) x[i][j] = ri;
+        else x[i][j] = __builtin_fmaf(kf[i], wv[j], ri);
+      }
+
+    // readout partial o_j over this wavefront's rows
     {
       float o8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float acc = 0.f;
+        float acc = __fmul_rn(qf[0], x[0][j]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(qf[i], x[i][j], acc);
-#pragma unroll
-        for (int s = 0; s < NB; ++s) acc += shfl_xor(acc, 32 >> s);
+        for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(qf[i], x[i][j], acc);
         o8[j] = acc;
       }
-      if (lr == 0) {
+      xtree<NB>(o8, lane);
+      const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
+      if (wrw == 1 && !kBypass) {
+        // one wavefront covers every row: its sums are the readout
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lds_o[wr * a.dv + j0 + j] = o8[j];
+        for (int s = 0; s < NSLOT; ++s) {
+          const float o = o8[s];
+          if (!(fabsf(o) <= 3.4e38f)) flags |= kStatusNonfinite;
+          if (writer) a.o[(size_t)tile * a.dv + j0 + xtree_col<NB>(s, lane)] = o;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s)
+          if (writer) L.op[wr * a.dv + j0 + xtree_col<NB>(s, lane)] = o8[s];
       }
     }
 
@@ -176,6 +403,9 @@ struct Decode {
       store_f32_chunk(cp, x);
       return;
     } else {
+      constexpr int qmax = Fmt<BITS>::qmax;
+      constexpr float qmaxf = (float)qmax;
+      constexpr float magic = Fmt<BITS>::magic;
       // yoked reference: the same recurrence on an fp32 tile; absmax comes from it
       float xr[kYoked ? 8 : 1][8];
       if constexpr (kYoked) {
@@ -183,91 +413,128 @@ struct Decode {
         load_f32_chunk(rp, xr);
         float wr_[8];
         if constexpr (MODEL == kGDN) {
-          const float al = a.alpha[tile], be = a.beta[tile];
-          float u[8];
+          float ones[8], dummy[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float t[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) t[i] = __fmul_rn(kf[i], xr[i][j]);
-            u[j] = rows_tree(tree8(t));
-          }
-          rows_tree_waves(u, lds_ur, wrw, wr, lr, j0, a.dv);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) wr_[j] = __fmul_rn(be, __fsub_rn(vf[j], __fmul_rn(al, u[j])));
+          for (int i = 0; i < 8; ++i) ones[i] = 1.f, dummy[i] = 0.f;
+          delta_w<8>(a, tile, xr, kf, ones, dummy, false, wr_, L.w, L.up + wrw * a.dv, wrw, wr, j0, lane, wave);
         } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) wr_[j] = vf[j];
+          load8(bf16, a.v, (size_t)tile * a.dv + j0, wr_);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            xr[i][j] = __builtin_fmaf(kf[i], wr_[j], __fmul_rn(dec[i], xr[i][j]));
+          for (int j = 0; j < 8; ++j) xr[i][j] = __builtin_fmaf(kf[i], wr_[j], __fmul_rn(dec[i], xr[i][j]));
         store_f32_chunk(rp, xr);
       }
 
       // scale rule per row of this lane's group
-      constexpr int qmax = (1 << (BITS - 1)) - 1;
-      constexpr float qmaxf = (float)qmax;
       float s_new[8], inv[8];
+      bool tiny = false, grew_any = true;
+      auto row_max = [&](int i) {
+        float m = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
+        if constexpr (SP::GL > 0) return group_max<SP::GL>(m);
+        else return group_max_rt(m, gl);
+      };
+      if (smode == kScalePersistent) {
+        const float trig_q = __fmul_rn(a.trigger, qmaxf);
+        float mx[8], over[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float m = 0.f;
+        for (int i = 0; i < 8; ++i) {
+          mx[i] = row_max(i);
+          s_new[i] = s_old[i];
+          // the sign of fl(m - thr) is the sign of m - thr
+          over[i] = __fsub_rn(mx[i], __fmul_rn(trig_q, s_old[i]));
+        }
+        grew_any = wave_any(max8(over) > 0.f);
+        if (grew_any) {
+          // the rows that outgrew their range take fl(m / qmax) in the storage dtype
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (kYoked) m = fmaxf(m, fabsf(xr[i][j]));
-          else m = fmaxf(m, fabsf(x[i][j]));
+          for (int i = 0; i < 8; ++i) {
+            const float ratio = mx[i] / qmaxf;
+            const float fresh = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
+            if (over[i] > 0.f) s_new[i] = fresh;
+          }
         }
-        if (gl >= 2) m = fmaxf(m, shfl_xor(m, 1));
-        if (gl >= 4) m = fmaxf(m, shfl_xor(m, 2));
-        if (gl >= 8) m = fmaxf(m, shfl_xor(m, 4));
-        if (gl >= 16) m = fmaxf(m, shfl_xor(m, 8));
-        const float ratio = m / qmaxf;
-        const float fresh = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
-        float sn = fresh;
-        if (a.smode == kScalePersistent) {
-          const float thr = __fmul_rn(__fmul_rn(a.trigger, qmaxf), s_old[i]);
-          sn = (m > thr) ? fresh : s_old[i];
+      } else {
+        // dynamic / yoked: fl(m / qmax) in the storage dtype, every row
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float ratio = row_max(i) / qmaxf;
+          s_new[i] = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
         }
-        if (isinf(sn)) flags |= kStatusScaleOverflow;
-        s_new[i] = sn;
-        inv[i] = (sn == 0.f) ? 0.f : 1.0f / sn;
       }
-
-      // requantize (+ BDR toward the update's sign)
-      int q[8][8];
-      const float lo = (float)(-(1 << (BITS - 1))), hi = qmaxf;
-      const float gate_k = __fadd_rn(0.5f, a.bdr_eps);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float gate = __fmul_rn(gate_k, s_new[i]);
+        const float sn = s_new[i];
+        inv[i] = (sn == 0.f) ? 0.f : (sf16 ? recip_f16val(sn) : 1.0f / sn);
+      }
+      {
+        // an infinite step (binary16 overflow) stores code 0; tiny steps need the clamp
+        const float smax = max8(s_new), imax = max8(inv);
+        if (!(smax <= 3.4e38f)) flags |= kStatusScaleOverflow;
+        tiny = !(smax <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float t = __builtin_fmaf(x[i][j], inv[i], kMagic) - kMagic;
-          if (t < lo || t > hi) flags |= kStatusClipped;
-          float c = fminf(fmaxf(t, lo), hi);
-          if constexpr (!kBypass) {
-            if (bdr && s_new[i] > 0.f) {
-              const float sg = (float)((kf[i] > 0.f) - (kf[i] < 0.f)) * (float)((wv[j] > 0.f) - (wv[j] < 0.f));
-              if (sg != 0.f) {
-                const float val = __fmul_rn(c, s_new[i]);
-                const bool rev = (sg > 0.f) ? (val < r[i][j]) : (val > r[i][j]);
-                if (rev) {
-                  const float cand = fminf(fmaxf(c + sg, lo), hi);
-                  const float err = fabsf(__fsub_rn(x[i][j], __fmul_rn(cand, s_new[i])));
-                  if (err <= gate) c = cand;
-                }
-              }
+      for (int i = 0; i < 8; ++i)
+        if (!(s_new[i] <= 3.4e38f)) inv[i] = 0.f;
+      // codes can leave the range only for tiny steps, yoked scales, or a
+      // persistent trigger above 1
+      const bool clamp = kYoked || wave_any(tiny) || (smode == kScalePersistent && a.trigger > 1.f);
+
+      // requantize: t = 1.5*2^23 + 2^(b-1) + RNE(x inv)   (+ BDR toward the update's sign)
+      const bool bdr = (FEAT == kFeatBdr) || (kYoked && a.bdr);
+      const float lo_t = 12582912.0f, hi_t = magic + qmaxf;
+      // BDR needs x after rounding; otherwise t overwrites x in place
+      float xk[(kKeepR && (FEAT == kFeatBdr || kYoked)) ? 8 : 1][8];
+      if constexpr (kKeepR && (FEAT == kFeatBdr || kYoked)) {
+        if (bdr) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xk[i][j] = x[i][j];
+        }
+      }
+      float (&t)[8][8] = x;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[i][j] = __builtin_fmaf(x[i][j], inv[i], magic);
+      if (clamp) {
+        bool clipped = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          clipped = clipped || max8(t[i]) > hi_t || min8(t[i]) < lo_t;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) t[i][j] = med3_nc(t[i][j], lo_t, hi_t);
+        }
+        if (clipped) flags |= kStatusClipped;
+      }
+      if constexpr (kKeepR && (FEAT == kFeatBdr || kYoked)) {
+        if (bdr) {
+          const float gate_k = __fadd_rn(0.5f, a.bdr_eps);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (!(s_new[i] > 0.f)) continue;
+            const float gate = __fmul_rn(gate_k, s_new[i]);
+            const float sk = (float)((kf[i] > 0.f) - (kf[i] < 0.f));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float sg = sk * (float)((wv[j] > 0.f) - (wv[j] < 0.f));
+              const float c = t[i][j] - magic;
+              const float val = __fmul_rn(c, s_new[i]);
+              const bool rev = (sg > 0.f && val < r[i][j]) || (sg < 0.f && val > r[i][j]);
+              const float cand = fminf(fmaxf(c + sg, -(float)(qmax + 1)), qmaxf);
+              const float err = fabsf(__fsub_rn(xk[i][j], __fmul_rn(cand, s_new[i])));
+              if (rev && err <= gate) t[i][j] = cand + magic;
             }
           }
-          q[i][j] = (int)c;
         }
       }
       Chunk<BITS> out;
-      pack(q, out);
+      pack_offset(t, out);
       store_chunk<BITS>(cp, out);
-      if ((lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);
+      const bool store_s = smode != kScalePersistent || grew_any;
+      if (store_s && (lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);
     }
   }
 
@@ -278,73 +545,119 @@ struct Decode {
     const HeadEntry he = a.heads[h];
     uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
     const int wrw = a.dk / WR;
-    float* lds_o = lds;                       // [wrw][dv]
-    float* lds_u = lds_o + wrw * a.dv;        // [wrw][dv]
-    float* lds_ur = lds_u + wrw * a.dv;       // [wrw][dv]
-    float* lds_z = lds_ur + wrw * a.dv;       // [kMaxCap] + [nwaves][kMaxCap]
+    const int nw = blockDim.x >> 6;
+    Lds L;
+    L.w = lds;                                // [nw][WC]
+    L.up = L.w + nw * WC;                     // [2][wrw][dv]
+    L.op = L.up + 2 * wrw * a.dv;             // [wrw][dv]
+    L.z = L.op + wrw * a.dv;                  // [kMaxCap] + [nw][kMaxCap]
     uint32_t flags = 0;
 
-    if constexpr (FEAT == kFeatBypass) bypass_decode_phase(a, he, tb, tile, lds_z, MODEL);
+    if constexpr (kBypass) bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
 
-    if constexpr (FEAT == kFeatF32) {
-      body<32>(a, he, tb, tile, lds_o, lds_u, lds_ur, flags);
+    if constexpr (kF32) {
+      body<32>(a, he, tb, tile, L, flags);
     } else {
       switch (he.bits) {
-        case 4: body<4>(a, he, tb, tile, lds_o, lds_u, lds_ur, flags); break;
-        case 6: body<6>(a, he, tb, tile, lds_o, lds_u, lds_ur, flags); break;
-        default: body<8>(a, he, tb, tile, lds_o, lds_u, lds_ur, flags); break;
+        case 4: body<4>(a, he, tb, tile, L, flags); break;
+        case 6: body<6>(a, he, tb, tile, L, flags); break;
+        default: body<8>(a, he, tb, tile, L, flags); break;
       }
     }
-    __syncthreads();
-    // combine readout partials over row-wavefronts, add the bypass term, store o
+    if (wrw > 1 || kBypass) {
+      __syncthreads();
+      // combine readout partials over row-wavefronts, add the bypass term, store o
+      combine_o(a, he, tb, tile, L, wrw, flags);
+    }
+    finish(a, tile, flags);
+  }
+
+  static __device__ __forceinline__ void combine_o(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
+                                                   int tile, const Lds& L, int wrw, uint32_t& flags) {
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
-      float acc = 0.f;
-      for (int q = 0; q < wrw; ++q) acc += lds_o[q * a.dv + j];
-      if constexpr (FEAT == kFeatBypass) {
+      float acc = L.op[j];
+      for (int q = 1; q < wrw; ++q) acc += L.op[q * a.dv + j];
+      if constexpr (kBypass) {
         const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
-        for (int c = 0; c <= a.n; ++c) acc = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), lds_z[c], acc);
+        for (int c = 0; c <= a.n; ++c) acc = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), L.z[c], acc);
       }
-      if (!isfinite(acc)) flags |= kStatusNonfinite;
+      if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
     }
+  }
+
+  static __device__ __forceinline__ void finish(const StepArgs& a, int tile, uint32_t flags) {
+    if (wave_any(flags != 0)) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) flags |= (uint32_t)__shfl_xor((int)flags, m, 64);
-    if (flags && (threadIdx.x & 63) == 0) atomicOr(a.status, flags);
+      for (int m = 32; m >= 1; m >>= 1) flags |= (uint32_t)__shfl_xor((int)flags, m, 64);
+      if ((threadIdx.x & 63) == 0) atomicOr(a.status, flags);
+    }
     if (tile == 0 && threadIdx.x == 0) {
       *a.hdr_t = a.t_next;
-      *a.hdr_n = (FEAT == kFeatBypass) ? a.n + 1 : 0;
+      *a.hdr_n = kBypass ? a.n + 1 : 0;
     }
   }
 };
 
-template <int MODEL, int CL, int FEAT>
+template <int MODEL, int CL, int FEAT, int SPEC>
 __global__ __launch_bounds__(512) void decode_kernel(StepArgs a) {
-  Decode<MODEL, CL, FEAT>::run(a);
+  Decode<MODEL, CL, FEAT, SPEC>::run(a);
+}
+
+// the specialised plain steps: at most 128 VGPRs, four wavefronts per SIMD
+template <int MODEL, int CL, int SPEC>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel_occ(StepArgs a) {
+  Decode<MODEL, CL, kFeatPlain, SPEC>::run(a);
+}
+
+template <int MODEL, int CL, int SPEC>
+DecodeFn decode_pick_feat(int feat) {
+  switch (feat) {
+    case kFeatPlain:
+      // the delta-rule step with binary16 persistent steps fits 128 VGPRs without
+      // spilling; the others keep their natural allocation (a spill reload waits for
+      // every outstanding load, which costs more than the lost occupancy)
+      if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, SPEC>;
+      else return decode_kernel<MODEL, CL, kFeatPlain, SPEC>;
+    case kFeatBdr: return decode_kernel<MODEL, CL, kFeatBdr, kSpecGeneric>;
+    case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass, SPEC>;
+    case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
+    default: return decode_kernel<MODEL, CL, kFeatF32, kSpecGeneric>;
+  }
 }
 
 template <int MODEL, int CL>
-DecodeFn decode_pick_feat(int feat) {
-  switch (feat) {
-    case kFeatPlain: return decode_kernel<MODEL, CL, kFeatPlain>;
-    case kFeatBdr: return decode_kernel<MODEL, CL, kFeatBdr>;
-    case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass>;
-    case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked>;
-    default: return decode_kernel<MODEL, CL, kFeatF32>;
+DecodeFn decode_pick_spec(int feat, int spec) {
+  if (feat != kFeatPlain && feat != kFeatBypass) spec = kSpecGeneric;
+  // group-32 specialisations use 4 column lanes, group-64 ones 8
+  if constexpr (CL == 4) {
+    switch (spec) {
+      case kSpecPersF16Bf16G32: return decode_pick_feat<MODEL, CL, kSpecPersF16Bf16G32>(feat);
+      case kSpecDynF16Bf16G32: return decode_pick_feat<MODEL, CL, kSpecDynF16Bf16G32>(feat);
+      default: break;
+    }
+  } else if constexpr (CL == 8) {
+    switch (spec) {
+      case kSpecDynF32Bf16G64: return decode_pick_feat<MODEL, CL, kSpecDynF32Bf16G64>(feat);
+      case kSpecDynF32F32G64: return decode_pick_feat<MODEL, CL, kSpecDynF32F32G64>(feat);
+      default: break;
+    }
   }
+  return decode_pick_feat<MODEL, CL, kSpecGeneric>(feat);
 }
 
 template <int MODEL>
-DecodeFn decode_pick_cl(int cl, int feat) {
+DecodeFn decode_pick_cl(int cl, int feat, int spec) {
   switch (cl) {
-    case 4: return decode_pick_feat<MODEL, 4>(feat);
-    case 8: return decode_pick_feat<MODEL, 8>(feat);
-    default: return decode_pick_feat<MODEL, 16>(feat);
+    case 4: return decode_pick_spec<MODEL, 4>(feat, spec);
+    case 8: return decode_pick_spec<MODEL, 8>(feat, spec);
+    default: return decode_pick_spec<MODEL, 16>(feat, kSpecGeneric);
   }
 }
 
-DecodeFn decode_retnet(int cl, int feat);
-DecodeFn decode_mamba2(int cl, int feat);
-DecodeFn decode_gla(int cl, int feat);
-DecodeFn decode_gdn(int cl, int feat);
+DecodeFn decode_retnet(int cl, int feat, int spec);
+DecodeFn decode_mamba2(int cl, int feat, int spec);
+DecodeFn decode_gla(int cl, int feat, int spec);
+DecodeFn decode_gdn(int cl, int feat, int spec);
 
 }  // namespace rsq

@@ -2,5 +2,5 @@
 #include "decode_impl.hpp"
 
 namespace rsq {
-DecodeFn decode_retnet(int cl, int feat) { return decode_pick_cl<kRetNet>(cl, feat); }
+DecodeFn decode_retnet(int cl, int feat, int spec) { return decode_pick_cl<kRetNet>(cl, feat, spec); }
 }  // namespace rsq

@@ -148,7 +148,9 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   if (G.threads > 512) return fail(RSQ_E_UNSUPPORTED, "d_k*d_v = %d exceeds 32768", c->d_k * c->d_v);
   if (c->model == RSQ_GDN && (c->d_k & (c->d_k - 1)))
     return fail(RSQ_E_UNSUPPORTED, "the delta rule needs a power-of-two d_k, got %d", c->d_k);
-  G.lds = (size_t)(3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64)) * sizeof(float);
+  // per-wave w broadcast, 2 x retrieval partials, readout partials, bypass projections
+  G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64)) *
+          sizeof(float);
 
   // layout
   if (c->gamma) {
@@ -398,7 +400,16 @@ rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const vo
   else if (st->bypass) feat = rsq::kFeatBypass;
   else if (st->cfg.scale_mode == RSQ_SCALE_YOKED) feat = rsq::kFeatYoked;
   else if (st->cfg.bdr) feat = rsq::kFeatBdr;
-  rsq::DecodeFn fn = rsq::decode_kernel_for(model, st->geo.cl, feat);
+  // compile-time specialisations of (scale mode, step dtype, input dtype)
+  const bool sf16 = st->cfg.scale_dtype == RSQ_F16, bf16 = st->cfg.in_dtype == RSQ_BF16;
+  const int sm = st->cfg.scale_mode;
+  const int g = st->cfg.group;
+  int spec = 0;
+  if (sm == RSQ_SCALE_PERSISTENT && sf16 && bf16 && g == 32) spec = 1;
+  else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && bf16 && g == 64) spec = 2;
+  else if (sm == RSQ_SCALE_DYNAMIC && sf16 && bf16 && g == 32) spec = 3;
+  else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && !bf16 && g == 64) spec = 4;
+  rsq::DecodeFn fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
   const rsq_status s = launch(fn, st, a, stream);
   if (s != RSQ_OK) return s;
   st->t += 1;

@@ -39,7 +39,7 @@ struct StepArgs {
 };
 
 typedef void (*DecodeFn)(StepArgs);
-DecodeFn decode_kernel_for(int model, int cl, int feat);
+DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
 DecodeFn readout_kernel_for(int cl);
 DecodeFn merge_kernel_for(int cl);
 
