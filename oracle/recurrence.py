@@ -395,8 +395,8 @@ def merge(st: OState, w, A: Arith = F32):
     M = |L| > fl(eps_L s); x = s_hat + L on M; requantize with BDR
     (sigma = sign(L) on M, reference r = s_hat); the residual L on not-M is
     replaced by its best rank-k approximation (SVD), stored as balanced fp16
-    factors U_k S_k^(1/2), V_k S_k^(1/2) with each U column's largest-magnitude
-    entry positive; n = k.
+    factors U_k S_k^(1/2), V_k S_k^(1/2) with each stored U column's
+    largest-magnitude entry (the first one on ties) positive; n = k.
     Returns (new state, diag with L, M, R and the singular values of R).
     """
     if st.U is None:
@@ -429,12 +429,13 @@ def merge(st: OState, w, A: Arith = F32):
         Uu, S, Vt = np.linalg.svd(R[ti], full_matrices=False)
         svals[ti] = S
         for j in range(k):
-            uc = Uu[:, j] * np.sqrt(S[j])
-            wc = Vt[j, :] * np.sqrt(S[j])
+            uc = f16_round(Uu[:, j] * np.sqrt(S[j]))
+            wc = f16_round(Vt[j, :] * np.sqrt(S[j]))
+            # sign fixed on the stored column (binary16 rounding is odd-symmetric)
             if uc[np.argmax(np.abs(uc))] < 0:
                 uc, wc = -uc, -wc
-            new.U[ti, :, j] = f16_round(uc)
-            new.W[ti, :, j] = f16_round(wc)
+            new.U[ti, :, j] = uc
+            new.W[ti, :, j] = wc
     new.n = k
     qd.update(L=L, M=M, R=R, svals=svals, x=x)
     return new, qd
