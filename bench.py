@@ -18,6 +18,7 @@ summaries when they were taken on the current kernel sources, else null.
 `cpu_baseline` times the CPU oracle (test infrastructure) on a bounded sample.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -30,15 +31,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+GROUP = 16          # launches per timed event pair
 METRIC = "quantized state-update steps/sec (batch*heads*steps) and achieved HBM GB/s vs peak"
 
 
+DECODE_SOURCES = ("decode_impl.hpp", "lane_ops.hpp", "rsq_device.hpp", "rsq_kernels.hpp", "decode_dispatch.hip",
+                  "decode_retnet.hip", "decode_mamba2.hip", "decode_gla.hip", "decode_gdn.hip")
+
+
 def kernel_source_hash():
+    """Hash of the sources that define the decode kernel (counter summaries are
+    only used while it matches)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_recurrent_state_rsq_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -53,26 +60,31 @@ def load_traffic(workload_name, bytes_per_launch):
     return d.get("hbm_bytes_per_launch"), d
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The oracle's canonical fp32 step on a bounded sample of tiles, on the host cores."""
+def cpu_baseline(w, tiles_per_worker=64, steps=256):
+    """The oracle's fp32-canonical step, as it stands, on a bounded sample of tiles.
+
+    One worker process per host core (at most 16), each with one BLAS thread,
+    steps `tiles_per_worker` tiles of the workload's shape for `steps` steps
+    (with bypass merges where the workload has them). Only the step loop is
+    timed; the rate is the sum of updates over the slowest worker's loop time.
+    """
     import multiprocessing as mp
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    tiles_per_worker, steps = 8, 4
     args = [(w, i, tiles_per_worker, steps) for i in range(cores)]
     ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
     with ctx.Pool(cores) as pool:
         done = pool.map(_oracle_worker, args)
-    wall = time.perf_counter() - t0
-    updates = sum(done)
-    return {"value": updates / wall, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
-            "sample": "%d worker processes x %d tiles x %d steps of the same workload "
-                      "(oracle fp32-canonical step, numpy, one thread each); %.1f s wall"
-                      % (cores, tiles_per_worker, steps, wall)}
+    updates = sum(u for u, _ in done)
+    loop_s = max(t for _, t in done)
+    return {"value": updates / loop_s, "unit": "state-updates/s", "cores": cores, "kind": "oracle",
+            "sample": "%d worker processes x %d tiles (%dx%d, the workload's heads cycled) x %d steps; "
+                      "oracle fp32-canonical step in numpy, one thread per process; slowest step loop %.1f s"
+                      % (cores, tiles_per_worker, w.d_k, w.d_v, steps, loop_s)}
 
 
 def _oracle_worker(a):
     os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
     w, wid, ntiles, steps = a
     import oracle
     from rsq_workloads import static_params, step_inputs
@@ -83,10 +95,60 @@ def _oracle_worker(a):
     hb = oracle.recurrence.tile_bits(w)
     st.bits = hb[np.arange(ntiles) % w.heads].astype(np.int32)
     t0 = time.perf_counter()
-    for inp in inps:
+    for t, inp in enumerate(inps, 1):
         st, o, d = oracle.step(st, inp, sw, oracle.F32, static)
-    _ = time.perf_counter() - t0
-    return ntiles * steps
+        if w.lrb_m and t % w.lrb_m == 0:
+            st, _ = oracle.merge(st, sw, oracle.F32)
+    return ntiles * steps, time.perf_counter() - t0
+
+
+def copy_reference(torch, nbytes=1 << 30, reps=10):
+    """Bandwidth of a plain device-to-device copy (read + write bytes / time)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes_per_copy": 2 * nbytes, "ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+class _HipEvents:
+    """HIP events (through the runtime PyTorch loaded) that the decode kernel's
+    dispatch records itself via rsq_decode_step_timed: they time each launch
+    on its own stream without putting marker commands between the launches."""
+
+    def __init__(self, n):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        P = ctypes.c_void_p
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        self.rt.hipEventDestroy.argtypes = [P]
+        self.ev = []
+        for _ in range(n):
+            e = P()
+            if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self):
+        for e in self.ev:
+            self.rt.hipEventDestroy(e)
+        self.ev = []
 
 
 def main():
@@ -99,6 +161,8 @@ def main():
     ap.add_argument("--warm", action="store_true", help="time one state set in place (cache-warm)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--min-set-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only time a plain 1 GiB device copy (the reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode step has no cross-GPU exchange (tiles shard "
@@ -107,6 +171,10 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"copy_reference": copy_reference(torch)}), flush=True)
+        return
     import bit_recurrent_state_rsq_amd as rsq
     from rsq_workloads import CONFIGS, head_bits_for, InputPool
 
@@ -114,6 +182,7 @@ def main():
     # the CPU baseline forks worker processes: do it before this process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(w)
     torch.cuda.set_device(0)
+    copy_ref = copy_reference(torch)
     hb = head_bits_for(w)
     kw = rsq.config_kwargs_from(w, head_bits=hb if w.mixed_bits else None)
     per_state = rsq.state_bytes(**kw)
@@ -135,40 +204,81 @@ def main():
     out = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
     cap = w.lrb_k + w.lrb_m if w.lrb_m else 0
 
-    def one_step(s, st):
-        d = dev[s % len(dev)]
-        st.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
+    stream = torch.cuda.current_stream()
+    # one bound launch per (state set, input step) pair used by the loops below
+    bound = {}
+
+    def step_fn(s):
+        key = (s % nsets, s % len(dev))
+        if key not in bound:
+            d = dev[key[1]]
+            bound[key] = states[key[0]].bind_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
+                                                  out=out, stream=stream)
+        return bound[key]
+
+    def after(s):
+        st = states[s % nsets]
         if cap and st.counters()[1] == cap:
-            st.merge_bypass()
+            st.merge_bypass(stream=stream)
 
     if args.warmup is None:
         args.warmup = max(64, 24 * nsets)
     for s in range(args.warmup):
-        one_step(s, states[s % nsets])
+        step_fn(s)()
+        after(s)
     torch.cuda.synchronize()
 
     K = args.steps
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # which timed steps are followed by a bypass merge (a state merges once its
+    # fill reaches k + m): the fill of every state evolves deterministically
+    merge_after = set()
+    if cap:
+        fill = [st.counters()[1] for st in states]
+        for s in range(K):
+            i = s % nsets
+            fill[i] += 1
+            if fill[i] == cap:
+                merge_after.add(s)
+                fill[i] = w.lrb_k
+    # decode-kernel durations: a start event rides on the first dispatch and a
+    # stop event on the last dispatch of each group of up to GROUP consecutive
+    # steps (events on every dispatch would stall the queue between launches);
+    # a group ends at a merge, so group times hold decode launches only
+    groups = []
+    g0 = 0
+    for s in range(K):
+        if s - g0 + 1 == GROUP or s in merge_after or s == K - 1:
+            groups.append((g0, s + 1))
+            g0 = s + 1
+    hip = _HipEvents(2 * len(groups))
+    calls = [step_fn(s) for s in range(K)]
+    ev_of = {}
+    for gi, (a0, a1) in enumerate(groups):
+        ev_of[a0] = [hip.ev[2 * gi], None]
+        ev_of.setdefault(a1 - 1, [None, None])[1] = hip.ev[2 * gi + 1]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        st = states[s % nsets]
-        d = dev[s % len(dev)]
-        ev[s][0].record(stream)
-        st.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out)
-        ev[s][1].record(stream)
-        if cap and st.counters()[1] == cap:
-            st.merge_bypass()
+        e = ev_of.get(s)
+        if e is None:
+            calls[s]()
+        else:
+            calls[s](e[0], e[1])
+        if s in merge_after:
+            states[s % nsets].merge_bypass(stream=stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if cap and [st.counters()[1] for st in states] != fill:
+        raise RuntimeError("bypass fill differs from the merge schedule")
+    group_ms = np.array([hip.elapsed(2 * gi, 2 * gi + 1) for gi in range(len(groups))])
+    group_n = np.array([a1 - a0 for a0, a1 in groups])
+    hip.destroy()
 
     bytes_step = rsq.workload_step_bytes(w.model, w.batch, hb, w.group, w.scale_dtype, w.d_k, w.d_v,
                                          w.in_dtype, w.lrb_k, w.lrb_m)
     updates = w.batch * w.heads * K
     value = updates / wall
-    mean_ms = float(kernel_ms.mean())
+    mean_ms = float(group_ms.sum() / group_n.sum())
     achieved = bytes_step / (mean_ms * 1e-3) / 1e9
     traffic, tinfo = load_traffic(w.name, bytes_step)
     flags = [st.get_status() for st in states[: min(4, nsets)]]
@@ -202,10 +312,15 @@ def main():
             "traffic": traffic,
         },
         "kernel": {"name": "rsq::decode_kernel", "mean_us": mean_ms * 1e3,
-                   "median_us": float(np.median(kernel_ms)) * 1e3,
+                   "median_us": float(np.median(group_ms / group_n)) * 1e3,
+                   "timing": "HIP events on the dispatches of the first and last launch of each "
+                             "group of up to %d consecutive decode steps in the timed region "
+                             "(groups end at bypass merges)" % GROUP,
+                   "merges_in_timed_region": len(merge_after),
                    "algorithmic_bytes_per_launch": bytes_step,
                    "hbm_gbs_wall": bytes_step * K / wall / 1e9},
         "status_flags": flags,
+        "copy_reference": copy_ref,
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu

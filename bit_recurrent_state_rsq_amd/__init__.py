@@ -127,11 +127,20 @@ class State:
         self.yoked = kw.get("scale_mode") == "yoked"
         self._sections = [self._tile_sections(hh) for hh in range(self.heads)]
 
-    def __del__(self):
+    def close(self):
+        """Free the host handle (the device buffer stays with its tensor)."""
         h = getattr(self, "h", None)
         if h is not None and h.value:
-            lib.rsq_state_free(h)
-            self.h = None
+            _abi.lib.rsq_state_free(h)
+        self.h = None
+
+    def __del__(self):
+        # at interpreter exit the binding may already be torn down; the handle
+        # is a small host allocation that the exiting process releases anyway
+        try:
+            self.close()
+        except (AttributeError, TypeError):
+            pass
 
     # ------------------------------------------------------------------ calls
     def _ptr(self, t, dtype, shape, name):
@@ -162,6 +171,35 @@ class State:
             self._ptr(alpha, torch.float32, ashape, "alpha"), self._ptr(beta, torch.float32, (B, H), "beta"),
             self._ptr(out, torch.float32, (B, H, dv), "o"), _stream_ptr(stream)))
         return out
+
+    def bind_step(self, q, k, v, alpha=None, beta=None, out=None, stream=None):
+        """Check the step's arguments once; return a callable that issues that step.
+
+        Each call of the returned function is one rsq_decode_step with the same
+        tensors (which it keeps alive) on the same stream, without re-checking
+        them: the lean form for a tight launch loop.
+        """
+        torch = _torch()
+        B, H, dk, dv = self.batch, self.heads, self.d_k, self.d_v
+        idt = torch.bfloat16 if self.in_bf16 else torch.float32
+        ashape = (B, H, dk) if self.model == "gla" else (B, H)
+        args = (self.h, self._ptr(q, idt, (B, H, dk), "q"), self._ptr(k, idt, (B, H, dk), "k"),
+                self._ptr(v, idt, (B, H, dv), "v"),
+                self._ptr(alpha, torch.float32, ashape, "alpha"), self._ptr(beta, torch.float32, (B, H), "beta"),
+                self._ptr(out, torch.float32, (B, H, dv), "o"), _stream_ptr(stream))
+        keep = (q, k, v, alpha, beta, out, stream)
+        f, ft = lib.rsq_decode_step, lib.rsq_decode_step_timed
+
+        def issue(start_event=None, stop_event=None, _keep=keep):
+            """start_event / stop_event: optional hipEvent_t handles (ctypes.c_void_p)
+            recorded by the decode kernel's own dispatch (rsq_decode_step_timed)."""
+            if start_event is None and stop_event is None:
+                code = f(*args)
+            else:
+                code = ft(*args, start_event, stop_event)
+            if code:
+                check(code)
+        return issue
 
     def merge_bypass(self, stream=None):
         check(lib.rsq_merge_bypass(self.h, _stream_ptr(stream)))

@@ -31,7 +31,8 @@ INIT_ZERO, ATTACH = 0, 1
 F_NONFINITE, F_SCALE_OVERFLOW, F_CLIPPED = 1, 2, 4
 
 EXPORTS = ["rsq_state_bytes", "rsq_state_alloc", "rsq_state_free", "rsq_state_layout",
-           "rsq_tile_sections", "rsq_state_counters", "rsq_decode_step", "rsq_merge_bypass",
+           "rsq_tile_sections", "rsq_state_counters", "rsq_decode_step", "rsq_decode_step_timed",
+           "rsq_merge_bypass",
            "rsq_readout", "rsq_get_status", "rsq_last_error", "rsq_abi_version"]
 
 
@@ -73,7 +74,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("librsq.so is not built (expected at %s); run "
-                          "`python -m bit_recurrent_state_rsq_amd.build`" % LIB_PATH)
+                          "`python bit_recurrent_state_rsq_amd/build.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pcfg = ctypes.POINTER(Config)
@@ -85,6 +86,7 @@ def _load():
         "rsq_tile_sections": (I32, [P, I32] + [ctypes.POINTER(SZ)] * 6 + [ctypes.POINTER(I32)]),
         "rsq_state_counters": (I32, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(I32)]),
         "rsq_decode_step": (I32, [P, P, P, P, P, P, P, P]),
+        "rsq_decode_step_timed": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "rsq_merge_bypass": (I32, [P, P]),
         "rsq_readout": (I32, [P, P, P, P]),
         "rsq_get_status": (I32, [P, ctypes.POINTER(ctypes.c_uint32), P]),

@@ -1,7 +1,9 @@
 """Build librsq.so (the HIP kernels and the C ABI of include/rsq.h) for gfx950.
 
-Run as `python -m bit_recurrent_state_rsq_amd.build`. Compiles every source in
-csrc/ with hipcc into the package directory. The library is always rebuilt.
+Run as `python bit_recurrent_state_rsq_amd/build.py` (a plain script: it does
+not import the package, which would load the library it is about to rebuild).
+Compiles every source in csrc/ with hipcc into the package directory. The
+library is always rebuilt.
 """
 import os
 import subprocess

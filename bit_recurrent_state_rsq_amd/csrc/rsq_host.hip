@@ -2,6 +2,7 @@
 // the handle (step count t, bypass fill n), kernel selection and launch on the
 // caller's stream, status word and error strings.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -44,8 +45,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Geometry {
   int cl, wr, wc, wrw, wcw, threads;
-  size_t lds;
+  size_t lds;         // decode / readout
+  size_t lds_merge;   // bypass merge (0 without a bypass)
 };
+
+constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
 
 uint64_t fnv1a(uint64_t h, const void* p, size_t n) {
   const uint8_t* b = static_cast<const uint8_t*>(p);
@@ -151,6 +155,10 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   // per-wave w broadcast, 2 x retrieval partials, readout partials, bypass projections
   G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64)) *
           sizeof(float);
+  G.lds_merge = p.bypass ? rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap) * sizeof(float) : 0;
+  if (G.lds_merge > kLdsBytes)
+    return fail(RSQ_E_UNSUPPORTED, "the bypass merge of a %d x %d tile with %d columns needs %zu bytes of LDS",
+                c->d_k, c->d_v, p.cap, G.lds_merge);
 
   // layout
   if (c->gamma) {
@@ -241,9 +249,22 @@ StepArgs base_args(rsq_state* st) {
   return a;
 }
 
-rsq_status launch(rsq::DecodeFn fn, const rsq_state* st, const StepArgs& a, void* stream) {
-  hipLaunchKernelGGL(fn, dim3(st->cfg.batch * st->cfg.heads), dim3(st->geo.threads), st->geo.lds,
-                     (hipStream_t)stream, a);
+rsq_status launch(rsq::DecodeFn fn, const rsq_state* st, const StepArgs& a, void* stream,
+                  void* ev_start = nullptr, void* ev_stop = nullptr, size_t lds = 0) {
+  const dim3 grid(st->cfg.batch * st->cfg.heads), block(st->geo.threads);
+  if (lds == 0) lds = st->geo.lds;
+  if (lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "raising the kernel's LDS limit");
+  }
+  if (ev_start || ev_stop) {
+    // the events ride on the dispatch packet itself: no marker enters the stream
+    hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, (hipStream_t)stream, (hipEvent_t)ev_start,
+                          (hipEvent_t)ev_stop, 0u, a);
+  } else {
+    hipLaunchKernelGGL(fn, grid, block, lds, (hipStream_t)stream, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return RSQ_OK;
@@ -376,6 +397,11 @@ rsq_status rsq_state_counters(const rsq_state* st, int64_t* t, int32_t* n) {
 
 rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, float* o, void* stream) {
+  return rsq_decode_step_timed(st, q, k, v, alpha, beta, o, stream, nullptr, nullptr);
+}
+
+rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* o, void* stream, void* start_event, void* stop_event) {
   if (!st) return fail(RSQ_E_INVALID, "state is NULL");
   if (!q || !k || !v || !o) return fail(RSQ_E_INVALID, "q, k, v and o must be non-NULL");
   const int model = st->cfg.model;
@@ -410,7 +436,7 @@ rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const vo
   else if (sm == RSQ_SCALE_DYNAMIC && sf16 && bf16 && g == 32) spec = 3;
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && !bf16 && g == 64) spec = 4;
   rsq::DecodeFn fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
-  const rsq_status s = launch(fn, st, a, stream);
+  const rsq_status s = launch(fn, st, a, stream, start_event, stop_event);
   if (s != RSQ_OK) return s;
   st->t += 1;
   if (st->bypass) st->n += 1;
@@ -424,7 +450,7 @@ rsq_status rsq_merge_bypass(rsq_state* st, void* stream) {
   a.t_next = st->t;
   rsq::DecodeFn fn = rsq::merge_kernel_for(st->geo.cl);
   if (!fn) return fail(RSQ_E_UNSUPPORTED, "no merge kernel for this configuration");
-  const rsq_status s = launch(fn, st, a, stream);
+  const rsq_status s = launch(fn, st, a, stream, nullptr, nullptr, st->geo.lds_merge);
   if (s != RSQ_OK) return s;
   st->n = st->cfg.lrb_k;
   return RSQ_OK;

@@ -42,6 +42,9 @@ typedef void (*DecodeFn)(StepArgs);
 DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
 DecodeFn readout_kernel_for(int cl);
 DecodeFn merge_kernel_for(int cl);
+// dynamic LDS (floats) of the merge kernel for a tile of d_k x d_v split into
+// wrw x wcw wavefronts with `cap` bypass columns
+size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap);
 
 // Decay of key row i of a tile (Table 1, A_t column).
 __device__ __forceinline__ float row_decay(const StepArgs& a, const HeadEntry& he, int model,

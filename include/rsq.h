@@ -206,6 +206,17 @@ rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const vo
                            const float* alpha, const float* beta, float* o, void* stream);
 
 /*
+ * rsq_decode_step for profiling: the step's decode kernel records
+ * start_event (a hipEvent_t, may be NULL) when it begins and stop_event when
+ * it ends. The timestamps come from the kernel's own dispatch, so no extra
+ * command enters the stream and back-to-back steps stay back to back. The
+ * events belong to the caller and must exist on the stream's device.
+ */
+rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, float* o, void* stream,
+                                 void* start_event, void* stop_event);
+
+/*
  * Low-Rank Bypass merge: L = U W^T; elements with |L_ij| > eps_L * s move
  * into the quantized state, which is requantized (with BDR when enabled,
  * toward sign(L_ij)); the rest is replaced by a rank-k approximation kept as

@@ -59,6 +59,8 @@ GOOD = dict(model="gdn", batch=2, heads=4, d_k=128, d_v=128, group=32, bits=4,
     (dict(d_k=256, d_v=256), _abi.RSQ_E_UNSUPPORTED),              # more than 32768 elements
     (dict(bits=32, bdr=True), _abi.RSQ_E_INVALID),
     (dict(head_bits=[4, 6, 8, 32]), _abi.RSQ_E_INVALID),
+    # the merge of a 1024 x 32 tile with 32 bypass columns needs more LDS than a CU has
+    (dict(model="gla", d_k=1024, d_v=32, lrb_k=16, lrb_m=16), _abi.RSQ_E_UNSUPPORTED),
 ])
 def test_invalid_configurations_are_rejected(change, code):
     kw = dict(GOOD)

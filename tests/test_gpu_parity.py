@@ -189,3 +189,129 @@ def test_full_bypass_refuses_a_decode_step():
     with pytest.raises(rsq.Error) as e:
         gpu_step(st, to_device(step_inputs(w, 4, static), w))
     assert e.value.code == rsq._abi.RSQ_E_BYPASS_FULL
+
+
+def test_bound_and_timed_steps_match_the_plain_call():
+    """State.bind_step and rsq_decode_step_timed run the same step as rsq_decode_step."""
+    import ctypes
+    import torch
+    w = CONFIGS[1].with_(batch=4)
+    a, b = make_state(w), make_state(w)
+    static = static_params(w)
+    rt = ctypes.CDLL("libamdhip64.so.7")
+    P = ctypes.c_void_p
+    rt.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+    rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+    rt.hipEventDestroy.argtypes = [P]
+    ev = [P(), P()]
+    for e in ev:
+        assert rt.hipEventCreate(ctypes.byref(e)) == 0
+    stream = torch.cuda.current_stream()
+    try:
+        for t in range(1, 5):
+            d = to_device(step_inputs(w, t, static), w)
+            o1 = gpu_step(a, d)
+            o2 = torch.empty_like(o1)
+            issue = b.bind_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=o2, stream=stream)
+            if t % 2:
+                issue(ev[0], ev[1])
+            else:
+                issue()
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2)
+            assert torch.equal(a.buf, b.buf)
+            if t % 2:
+                ms = ctypes.c_float()
+                assert rt.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+                assert 0.0 < ms.value < 1000.0
+        assert a.counters() == b.counters() == (4, 0)
+    finally:
+        for e in ev:
+            rt.hipEventDestroy(e)
+
+
+def _merge_checker(w, results):
+    """Teacher-forced check of rsq_merge_bypass: the oracle merges the GPU's
+    pre-merge state of the sampled tiles. Codes and step sizes must match
+    outside the decision windows; the GPU's bypass factors must satisfy the
+    Eckart-Young bound on the oracle's residual (the factors of a rank-k
+    truncation are not unique, their product's error is)."""
+    def check(st, t, tiles, tally):
+        sw = sub_workload(w, tiles)
+        _, n = st.counters()
+        pre = st.read_tiles(tiles)
+        ost = to_oracle(pre, w, tiles, n)
+        ost.bits = tile_bits(w, tiles)
+        new, md = oracle.merge(ost, sw, oracle.F32)
+        st.merge_bypass()
+        post = st.read_tiles(tiles)
+        near, gnear = md["near"], md["group_near"]
+        diff = post["codes"] != new.codes
+        bad = diff & ~near
+        sbad = (post["scales"] != new.scales) & ~gnear
+        tally.elements += diff.size
+        tally.forgiven += int((diff & near).sum())
+        tally.mismatch += int(bad.sum()) + int(sbad.sum())
+        assert not bad.any(), "merge after step %d: codes differ at %s" % (t, np.argwhere(bad)[:4].tolist())
+        assert not sbad.any(), "merge after step %d: step sizes differ" % t
+        k = w.lrb_k
+        assert st.counters()[1] == k
+        U = post["U"].astype(np.float64)
+        W = post["W"].astype(np.float64)
+        assert not U[:, :, k:].any() and not W[:, :, k:].any(), "columns past k must be empty"
+        worst = 0.0
+        for ti in range(U.shape[0]):
+            sv = md["svals"][ti]
+            tail = np.sqrt(np.sum(sv[k:] ** 2))
+            err = np.linalg.norm(md["R"][ti] - U[ti, :, :k] @ W[ti, :, :k].T)
+            bound = (1 + 1e-3) * tail + 2.0 ** -10 * np.sum(sv[:k]) + 1e-12
+            assert err <= bound, "merge after step %d tile %d: |R - UW^T| %g > %g" % (t, ti, err, bound)
+            worst = max(worst, err / tail - 1 if tail > 0 else 0.0)
+            if k:
+                col = U[ti, :, :k]
+                top = col[np.argmax(np.abs(col), axis=0), np.arange(k)]
+                assert np.all(top >= 0), "U columns must have a positive largest entry"
+        results.append(worst)
+    return check
+
+
+def test_cfg3_gla_merges_match_oracle():
+    """Decode steps and four bypass merges of the GLA workload, teacher-forced."""
+    w = CONFIGS[3]
+    steps = w.lrb_k + w.lrb_m + 3 * w.lrb_m
+    merges = []
+    tally, st = run_parity(w, steps, check_steps=range(1, steps + 1), tiles=_sample_tiles(w, 4),
+                           merge_check=_merge_checker(w, merges))
+    tally.check()
+    assert len(merges) == 4
+    log("merge: worst Eckart-Young excess %.2e" % max(merges))
+
+
+def test_cfg3_gla_full_horizon_with_merges():
+    """The full 1024-step GLA workload: every merge checked on the sampled tiles."""
+    w = CONFIGS[3]
+    merges = []
+    checks = [1, 2, 20, 21, 37, 300, 517, 1000, w.steps]
+    tally, st = run_parity(w, w.steps, check_steps=checks, tiles=_sample_tiles(w, 2),
+                           merge_check=_merge_checker(w, merges))
+    tally.check()
+    assert len(merges) == (w.steps - w.lrb_k) // w.lrb_m
+    log("%d merges, worst Eckart-Young excess %.2e" % (len(merges), max(merges)))
+
+
+@pytest.mark.parametrize("model,bits,g,mode,sdt,dk,dv,k,m,bdr", [
+    ("retnet", 4, 32, "dynamic", "f16", 128, 128, 2, 5, True),
+    ("mamba2", 8, 64, "dynamic", "f32", 128, 64, 4, 8, False),
+    ("gla", 6, 16, "persistent", "f16", 128, 64, 3, 4, True),
+    ("gla", 4, 128, "dynamic", "f16", 64, 128, 1, 3, True),
+    ("retnet", 8, 32, "dynamic", "f32", 256, 32, 0, 4, True),
+])
+def test_merge_variants(model, bits, g, mode, sdt, dk, dv, k, m, bdr):
+    base = {"retnet": CONFIGS[0], "mamba2": CONFIGS[2], "gla": CONFIGS[3]}[model]
+    w = base.with_(batch=2, heads=3, d_k=dk, d_v=dv, bits=bits, group=g, scale_mode=mode, scale_dtype=sdt,
+                   lrb_k=k, lrb_m=m, lrb_eps=0.5, bdr=bdr, bdr_eps=0.5, in_dtype="bf16", mixed_bits=None)
+    merges = []
+    steps = k + 3 * m
+    tally, st = run_parity(w, steps, check_steps=range(1, steps + 1), merge_check=_merge_checker(w, merges))
+    tally.check()
+    assert len(merges) == 3
