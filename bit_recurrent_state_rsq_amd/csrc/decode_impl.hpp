@@ -49,7 +49,11 @@ struct Fmt {
   static constexpr float F = BITS == 4 ? 16.f : BITS == 6 ? 4.f : 1.f;   // unpacked value = F * code
   static constexpr float invF = 1.f / F;
   static constexpr int qmax = (1 << (BITS - 1)) - 1;
-  static constexpr float magic = 12582912.0f + (float)(1 << (BITS - 1));  // 1.5*2^23 + 2^(b-1)
+  // t = fma(x, inv, magic) rounds x*inv once, at unit spacing, to magic + RNE(x*inv).
+  // Its low byte is then the code as packing wants it: offset binary c + 8 for
+  // 4 bits (a clean nibble), two's complement c mod 256 for 6 and 8 bits.
+  static constexpr float magic = BITS == 4 ? 12582912.0f + 8.0f : 12582912.0f;
+  static constexpr float lo_t = magic - (float)(qmax + 1), hi_t = magic + (float)qmax;
   // products c * (k s) stay exact in float32 (|c| < 2^(b-1), k s has 19 bits)
   static constexpr bool kExactPairs = BITS <= 6;
 };
@@ -93,44 +97,55 @@ __device__ __forceinline__ void unpack_scaled(const Chunk<6>& ch, float c[8][8])
   }
 }
 
-// ---------------------------------------------------------------- pack offset codes
-// t holds 1.5*2^23 + 2^(b-1) + c; its low byte is the offset-binary code.
-__device__ __forceinline__ uint32_t gather_low_bytes(float a, float b, float c, float d) {
-  const uint32_t ab = __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x0c0c0400u);
-  const uint32_t cd = __builtin_amdgcn_perm(__float_as_uint(d), __float_as_uint(c), 0x0c0c0400u);
-  return ab | (cd << 16);
+// ---------------------------------------------------------------- pack codes from t
+// t holds magic + c (Fmt): its low byte is the code in the form packing uses.
+// Bytes [a.b0, b.b0, 0, 0] and [0, 0, c.b0, d.b0].
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x0c0c0400u); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t c, uint32_t d) { return __builtin_amdgcn_perm(d, c, 0x04000c0cu); }
+__device__ __forceinline__ uint32_t low_bytes(float a, float b, float c, float d) {
+  return lo_pair(__float_as_uint(a), __float_as_uint(b)) | hi_pair(__float_as_uint(c), __float_as_uint(d));
 }
+// (a & m) | (b & ~m)
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
 
-__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<4>& ch) {
+// 4 bits: byte k of word r = nibble(col k) | nibble(col k+4) << 4, two's
+// complement. From offset-binary nibbles (bits 4-7 of each low byte clear):
+// one shift-or per byte pair, two byte gathers and one XOR with 0x88.
+__device__ __forceinline__ void pack_t(const float t[8][8], Chunk<4>& ch) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const uint32_t lo = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
-    const uint32_t hi = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
-    ch.w[r] = (lo | (hi << 4)) ^ 0x88888888u;     // offset binary -> two's complement nibbles
+    uint32_t p[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = (__float_as_uint(t[r][k + 4]) << 4) | __float_as_uint(t[r][k]);
+    ch.w[r] = (lo_pair(p[0], p[1]) | hi_pair(p[2], p[3])) ^ 0x88888888u;
   }
 }
 
-__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<8>& ch) {
+// 8 bits: the low bytes are the codes
+__device__ __forceinline__ void pack_t(const float t[8][8], Chunk<8>& ch) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    ch.w[2 * r] = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]) ^ 0x80808080u;
-    ch.w[2 * r + 1] = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]) ^ 0x80808080u;
+    ch.w[2 * r] = low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
+    ch.w[2 * r + 1] = low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
   }
 }
 
-__device__ __forceinline__ void pack_offset(const float t[8][8], Chunk<6>& ch) {
-  uint32_t L[8], H[8];   // offset codes u = c + 32, one per byte
+// 6 bits: word r (r < 8) holds the high 4 bits of the codes like the 4-bit
+// layout; word 8+p holds the low 2 bits of rows 2p and 2p+1 (byte k: col k,
+// col k+4, then the same of the next row, 2 bits each from the bottom)
+__device__ __forceinline__ void pack_t(const float t[8][8], Chunk<6>& ch) {
+  uint32_t L[8], H[8];   // two's complement code bytes of columns 0-3 and 4-7
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    L[r] = gather_low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
-    H[r] = gather_low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
-    // high nibble of the two's complement code: (u >> 2) ^ 8
-    ch.w[r] = (((L[r] >> 2) & 0x0F0F0F0Fu) | ((H[r] << 2) & 0xF0F0F0F0u)) ^ 0x88888888u;
+    L[r] = low_bytes(t[r][0], t[r][1], t[r][2], t[r][3]);
+    H[r] = low_bytes(t[r][4], t[r][5], t[r][6], t[r][7]);
+    ch.w[r] = bfi(0x0F0F0F0Fu, L[r] >> 2, H[r] << 2);
   }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t m = 0x03030303u;
-    ch.w[8 + p] = (L[2 * p] & m) | ((H[2 * p] & m) << 2) | ((L[2 * p + 1] & m) << 4) | ((H[2 * p + 1] & m) << 6);
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t x = bfi(0x03030303u, L[2 * q], H[2 * q] << 2);
+    const uint32_t y = bfi(0x03030303u, L[2 * q + 1], H[2 * q + 1] << 2);
+    ch.w[8 + q] = bfi(0x0F0F0F0Fu, x, y << 4);
   }
 }
 
@@ -303,8 +318,10 @@ struct Decode {
     const int rho = (int)(__builtin_bitreverse32((uint32_t)lr) >> (32 - NB));
     const int i0 = wr * WR + 8 * rho;
     const int j0 = wc * WC + 8 * lc;
-    const int G = j0 / a.group;
-    const int gl = a.group >> 3;        // lanes per group (1..16)
+    // group sizes are powers of two: the group index is a shift
+    const int glog = SP::GL > 0 ? 3 + __builtin_ctz(SP::GL > 0 ? SP::GL : 1) : 31 - __builtin_clz(a.group);
+    const int G = j0 >> glog;
+    const int gl = SP::GL > 0 ? SP::GL : (a.group >> 3);   // lanes per group (1..16)
     constexpr float F = kF32 ? 1.f : Fmt<BITS == 32 ? 8 : BITS>::F;
     constexpr float invF = 1.f / F;
 
@@ -432,7 +449,7 @@ struct Decode {
       bool tiny = false, grew_any = true;
       auto row_max = [&](int i) {
         float m = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
-        if constexpr (SP::GL > 0) return group_max<SP::GL>(m);
+        if constexpr (SP::GL > 0) return group_absmax<SP::GL>(m);
         else return group_max_rt(m, gl);
       };
       if (smode == kScalePersistent) {
@@ -463,27 +480,29 @@ struct Decode {
           s_new[i] = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
         }
       }
+      // the common case, every step of the wavefront normal and finite, needs
+      // neither the zero / overflow handling nor the clamp
+      const float s_lo = min8(s_new), s_hi = max8(s_new);
+      const bool regular = sf16 ? (s_lo >= 0x1p-14f && s_hi <= 65504.f) : (s_lo >= 0x1p-100f && s_hi <= 0x1p100f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float sn = s_new[i];
-        inv[i] = (sn == 0.f) ? 0.f : (sf16 ? recip_f16val(sn) : 1.0f / sn);
-      }
-      {
-        // an infinite step (binary16 overflow) stores code 0; tiny steps need the clamp
-        const float smax = max8(s_new), imax = max8(inv);
-        if (!(smax <= 3.4e38f)) flags |= kStatusScaleOverflow;
-        tiny = !(smax <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
-      }
+      for (int i = 0; i < 8; ++i) inv[i] = sf16 ? recip_f16val(s_new[i]) : 1.0f / s_new[i];
+      if (!wave_all(regular)) {
+        // a zero step, or an infinite one (binary16 overflow), stores code 0;
+        // tiny steps need the clamp
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (!(s_new[i] <= 3.4e38f)) inv[i] = 0.f;
+        for (int i = 0; i < 8; ++i)
+          if (s_new[i] == 0.f || !(s_new[i] <= 3.4e38f)) inv[i] = 0.f;
+        const float imax = max8(inv);
+        if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
+        tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
+      }
       // codes can leave the range only for tiny steps, yoked scales, or a
       // persistent trigger above 1
       const bool clamp = kYoked || wave_any(tiny) || (smode == kScalePersistent && a.trigger > 1.f);
 
       // requantize: t = 1.5*2^23 + 2^(b-1) + RNE(x inv)   (+ BDR toward the update's sign)
       const bool bdr = (FEAT == kFeatBdr) || (kYoked && a.bdr);
-      const float lo_t = 12582912.0f, hi_t = magic + qmaxf;
+      constexpr float lo_t = Fmt<BITS>::lo_t, hi_t = Fmt<BITS>::hi_t;
       // BDR needs x after rounding; otherwise t overwrites x in place
       float xk[(kKeepR && (FEAT == kFeatBdr || kYoked)) ? 8 : 1][8];
       if constexpr (kKeepR && (FEAT == kFeatBdr || kYoked)) {
@@ -531,7 +550,7 @@ struct Decode {
         }
       }
       Chunk<BITS> out;
-      pack_offset(t, out);
+      pack_t(t, out);
       store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
       if (store_s && (lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);

@@ -78,6 +78,21 @@ __device__ __forceinline__ float max_nc(float a, float b) {
   return m;
 }
 
+// max over the GL lanes of a scale group of values that are >= 0 (absolute
+// values): their bit patterns order like the values, so an integer max does
+// it, and the compiler folds each lane exchange (DPP) into the max itself.
+// The groups are the low lane bits; after the quad steps every lane of a quad
+// holds the quad's max, so the half-row and row mirrors complete 8 and 16.
+template <int GL>
+__device__ __forceinline__ float group_absmax(float m) {
+  uint32_t u = __float_as_uint(m);
+  if constexpr (GL >= 2) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false));
+  if constexpr (GL >= 4) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, false));
+  if constexpr (GL >= 8) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, false));
+  if constexpr (GL >= 16) u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x140, 0xF, 0xF, false));
+  return __uint_as_float(u);
+}
+
 // max over the GL lanes of a scale group (GL in 1, 2, 4, 8, 16: the low lane bits)
 template <int GL>
 __device__ __forceinline__ float group_max(float m) {
