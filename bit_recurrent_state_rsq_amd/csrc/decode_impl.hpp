@@ -453,23 +453,31 @@ struct Decode {
         else return group_max_rt(m, gl);
       };
       if (smode == kScalePersistent) {
+        // A group grows when its absmax m exceeds thr = fl(fl(trigger qmax) s):
+        // exactly when some lane's own maximum does (thr is the same on every
+        // lane of the group), so the exchange for the group maximum is only
+        // needed on a step where some group of the wavefront grows.
         const float trig_q = __fmul_rn(a.trigger, qmaxf);
-        float mx[8], over[8];
+        float lm[8], thr[8], over[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          mx[i] = row_max(i);
+          lm[i] = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
           s_new[i] = s_old[i];
+          thr[i] = __fmul_rn(trig_q, s_old[i]);
           // the sign of fl(m - thr) is the sign of m - thr
-          over[i] = __fsub_rn(mx[i], __fmul_rn(trig_q, s_old[i]));
+          over[i] = __fsub_rn(lm[i], thr[i]);
         }
         grew_any = wave_any(max8(over) > 0.f);
         if (grew_any) {
           // the rows that outgrew their range take fl(m / qmax) in the storage dtype
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float ratio = mx[i] / qmaxf;
+            float m;
+            if constexpr (SP::GL > 0) m = group_absmax<SP::GL>(lm[i]);
+            else m = group_max_rt(lm[i], gl);
+            const float ratio = m / qmaxf;
             const float fresh = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
-            if (over[i] > 0.f) s_new[i] = fresh;
+            if (m > thr[i]) s_new[i] = fresh;
           }
         }
       } else {
