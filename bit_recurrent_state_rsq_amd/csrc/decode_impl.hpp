@@ -46,7 +46,9 @@ namespace rsq {
 
 template <int BITS>
 struct Fmt {
-  static constexpr float F = BITS == 4 ? 16.f : BITS == 6 ? 4.f : 1.f;   // unpacked value = F * code
+  // unpacked value = F * code: 4-bit codes convert straight to c/16
+  // (v_cvt_off_f32_i4), 6-bit ones assemble to 4c, 8-bit ones are c
+  static constexpr float F = BITS == 4 ? 0.0625f : BITS == 6 ? 4.f : 1.f;
   static constexpr float invF = 1.f / F;
   static constexpr int qmax = (1 << (BITS - 1)) - 1;
   // t = fma(x, inv, magic) rounds x*inv once, at unit spacing, to magic + RNE(x*inv).
@@ -59,16 +61,29 @@ struct Fmt {
 };
 
 // ---------------------------------------------------------------- unpack to F*c
+// c/16 of the two's complement nibble in bits 0-3 of byte B of w
+template <int B>
+__device__ __forceinline__ float cvt_off_byte(uint32_t w) {
+  float r;
+  if constexpr (B == 0) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w));
+  else if constexpr (B == 1) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w));
+  else if constexpr (B == 2) asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w));
+  else asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w));
+  return r;
+}
+
 __device__ __forceinline__ void unpack_scaled(const Chunk<4>& ch, float c[8][8]) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const uint32_t lo = (ch.w[r] << 4) & 0xF0F0F0F0u;
-    const uint32_t hi = ch.w[r] & 0xF0F0F0F0u;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      c[r][b] = (float)(int8_t)(lo >> (8 * b));
-      c[r][b + 4] = (float)(int8_t)(hi >> (8 * b));
-    }
+    const uint32_t w = ch.w[r], hi = w >> 4;   // columns 0-3 in the low nibbles, 4-7 in the high ones
+    c[r][0] = cvt_off_byte<0>(w);
+    c[r][1] = cvt_off_byte<1>(w);
+    c[r][2] = cvt_off_byte<2>(w);
+    c[r][3] = cvt_off_byte<3>(w);
+    c[r][4] = cvt_off_byte<0>(hi);
+    c[r][5] = cvt_off_byte<1>(hi);
+    c[r][6] = cvt_off_byte<2>(hi);
+    c[r][7] = cvt_off_byte<3>(hi);
   }
 }
 
@@ -342,18 +357,28 @@ struct Decode {
     load8(bf16, a.k, (size_t)tile * a.dk + i0, kf);
     decays(a, he, tile, i0, dec);
 
-    // per-row multipliers: c1/F (decay) and k s / F (retrieval)
+    // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
+    // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
+    // by F = 4 (6 bits) unless the quotient is subnormal; F = 1 is no-op.
+    constexpr bool kUp = !kF32 && BITS == 4, kDown = !kF32 && BITS == 6;
     float c1p[8], kap[8], smul[8];
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float c1 = kF32 ? dec[i] : __fmul_rn(dec[i], s_old[i]);
-      c1p[i] = __fmul_rn(c1, invF);
-      if constexpr (!kF32) bad = bad || subnormal(c1p[i]);
+      c1p[i] = (kUp || kDown) ? __fmul_rn(c1, invF) : c1;
+      if constexpr (kDown) bad = bad || subnormal(c1p[i]);
+      if constexpr (kUp) {
+        if (!sf16) bad = bad || !(fabsf(c1p[i]) <= 3.4e38f);
+      }
       smul[i] = kF32 ? 1.f : s_old[i];
       if constexpr (MODEL == kGDN && !kF32) {
-        kap[i] = __fmul_rn(__fmul_rn(kf[i], s_old[i]), invF);
-        bad = bad || subnormal(kap[i]);
+        const float ks = __fmul_rn(kf[i], s_old[i]);
+        kap[i] = (kUp || kDown) ? __fmul_rn(ks, invF) : ks;
+        if constexpr (kDown) bad = bad || subnormal(kap[i]);
+        if constexpr (kUp) {
+          if (!sf16) bad = bad || !(fabsf(kap[i]) <= 3.4e38f);
+        }
       }
     }
     const bool fast = !wave_any(bad) && (kF32 || MODEL != kGDN || (bf16 && sf16));
