@@ -174,6 +174,28 @@ __device__ __forceinline__ float recip_f16val(float s) {
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 __device__ __forceinline__ bool wave_all(bool p) { return __builtin_amdgcn_ballot_w64(!p) == 0; }
 
+// q[i] = fl(m[i] / Q) for Q = 7, 31, 127 and m >= 0: y = fl(m RN(1/Q)), then
+// one FMA correction y + fl(m - y Q) RN(1/Q). That is the correctly rounded
+// quotient for every m in [2^-100, 2^100] and for m = 0 (checked for all
+// float32 m in [1, 2) for each Q; power-of-two scaling carries it over the
+// range). Outside it, and for NaN, the wavefront divides.
+template <int Q>
+__device__ __forceinline__ void div_qmax(const float m[8], float q[8]) {
+  constexpr float qf = (float)Q, zi = 1.0f / (float)Q;
+  const float lo = min8(m), hi = max8(m);
+  if (wave_all(hi <= 0x1p100f && (lo >= 0x1p-100f || lo == 0.f))) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = __fmul_rn(m[i], zi);
+      const float r = __builtin_fmaf(-y, qf, m[i]);
+      q[i] = __builtin_fmaf(r, zi, y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = m[i] / qf;
+  }
+}
+
 // m / F (F a small power of two) is exact unless the quotient is subnormal
 __device__ __forceinline__ bool subnormal(float m) { return __builtin_amdgcn_class(m, 0x90) != 0; }
 
@@ -495,23 +517,27 @@ struct Decode {
         grew_any = wave_any(max8(over) > 0.f);
         if (grew_any) {
           // the rows that outgrew their range take fl(m / qmax) in the storage dtype
+          float m[8], ratio[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            float m;
-            if constexpr (SP::GL > 0) m = group_absmax<SP::GL>(lm[i]);
-            else m = group_max_rt(lm[i], gl);
-            const float ratio = m / qmaxf;
-            const float fresh = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
-            if (m > thr[i]) s_new[i] = fresh;
+            if constexpr (SP::GL > 0) m[i] = group_absmax<SP::GL>(lm[i]);
+            else m[i] = group_max_rt(lm[i], gl);
+          }
+          div_qmax<qmax>(m, ratio);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float fresh = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
+            if (m[i] > thr[i]) s_new[i] = fresh;
           }
         }
       } else {
         // dynamic / yoked: fl(m / qmax) in the storage dtype, every row
+        float m[8], ratio[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float ratio = row_max(i) / qmaxf;
-          s_new[i] = sf16 ? __half2float(__float2half_rn(ratio)) : ratio;
-        }
+        for (int i = 0; i < 8; ++i) m[i] = row_max(i);
+        div_qmax<qmax>(m, ratio);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_new[i] = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
       }
       // the common case, every step of the wavefront normal and finite, needs
       // neither the zero / overflow handling nor the clamp
