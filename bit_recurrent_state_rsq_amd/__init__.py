@@ -25,7 +25,7 @@ from . import codec
 from .accounting import step_bytes_per_tile, workload_step_bytes
 
 __all__ = ["State", "Error", "state_bytes", "make_config", "step_bytes_per_tile",
-           "workload_step_bytes"]
+           "workload_step_bytes", "allocate_head_bits"]
 
 
 def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
@@ -77,6 +77,21 @@ def state_bytes(**kw) -> int:
     n = ctypes.c_size_t()
     check(lib.rsq_state_bytes(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def allocate_head_bits(decay_sq: Sequence[float], ranges: Sequence[float], mean_bits: float):
+    """Per-head widths in {4, 6, 8} with mean at most mean_bits that minimise
+    sum_h range_h^2 / (1 - decay_sq_h) / (2^(b_h-1) - 1)^2 (rsq_allocate_head_bits).
+    decay_sq[h] = E[a_t^2] of head h's decay; ranges[h] = its typical group absmax."""
+    d = np.ascontiguousarray(decay_sq, dtype=np.float32).reshape(-1)
+    r = np.ascontiguousarray(ranges, dtype=np.float32).reshape(-1)
+    if d.size != r.size:
+        raise ValueError("decay_sq and ranges must have one entry per head")
+    out = np.zeros(max(d.size, 1), dtype=np.int32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    check(lib.rsq_allocate_head_bits(d.ctypes.data_as(fp), r.ctypes.data_as(fp), int(d.size),
+                                     float(mean_bits), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return [int(b) for b in out[:d.size]]
 
 
 def _torch():

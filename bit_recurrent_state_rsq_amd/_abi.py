@@ -33,7 +33,7 @@ F_NONFINITE, F_SCALE_OVERFLOW, F_CLIPPED = 1, 2, 4
 EXPORTS = ["rsq_state_bytes", "rsq_state_alloc", "rsq_state_free", "rsq_state_layout",
            "rsq_tile_sections", "rsq_state_counters", "rsq_decode_step", "rsq_decode_step_timed",
            "rsq_merge_bypass",
-           "rsq_readout", "rsq_get_status", "rsq_last_error", "rsq_abi_version"]
+           "rsq_readout", "rsq_get_status", "rsq_last_error", "rsq_abi_version", "rsq_allocate_head_bits"]
 
 
 class Config(ctypes.Structure):
@@ -92,6 +92,8 @@ def _load():
         "rsq_get_status": (I32, [P, ctypes.POINTER(ctypes.c_uint32), P]),
         "rsq_last_error": (ctypes.c_char_p, []),
         "rsq_abi_version": (I32, []),
+        "rsq_allocate_head_bits": (I32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), I32,
+                                         ctypes.c_float, ctypes.POINTER(I32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -477,6 +478,53 @@ rsq_status rsq_get_status(rsq_state* st, uint32_t* flags, void* stream) {
   hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, hs, dev);
   if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "status clear");
   if ((e = hipStreamSynchronize(hs)) != hipSuccess) return hip_fail(e, "stream sync");
+  return RSQ_OK;
+}
+
+// Decay-aware per-head widths ("Low-Bit Recurrent States in Hybrid Language
+// Models", abstract: distortion weights from the observability Gramian with
+// normalised state ranges). Written out for the widths stored here:
+//  * an error put into a state that decays by a_t per step keeps contributing
+//    sum_t E[a^2]^t = 1 / (1 - E[a^2]) of its energy to later states;
+//  * a b-bit symmetric step for range rho is rho / (2^(b-1) - 1), and the
+//    rounding error energy scales with its square;
+// so head h at width b costs w_h / (2^(b-1) - 1)^2, w_h = rho_h^2 / (1 - E[a_h^2]).
+// Every upgrade (4->6, 6->8) costs 2 bits and a head's savings shrink as it
+// widens (1/7^2 - 1/31^2 > 1/31^2 - 1/127^2), so taking upgrades largest
+// saving first while the budget lasts minimises the total. Sorting all 2H
+// upgrades by (saving desc, head asc, level asc) gives that order in
+// O(H log H): a head's second upgrade never sorts before its first.
+rsq_status rsq_allocate_head_bits(const float* decay_sq, const float* range, int32_t heads,
+                                  float mean_bits, int32_t* bits_out) {
+  if (!decay_sq || !range || !bits_out) return fail(RSQ_E_INVALID, "NULL argument");
+  if (heads < 1 || heads > (1 << 20)) return fail(RSQ_E_INVALID, "heads = %d out of [1, 2^20]", heads);
+  if (!(mean_bits >= 4.f && mean_bits <= 8.f)) return fail(RSQ_E_INVALID, "mean_bits must be in [4, 8]");
+  struct Upgrade {
+    double gain;
+    int32_t head, level;
+  };
+  const double qsq[3] = {7.0 * 7.0, 31.0 * 31.0, 127.0 * 127.0};  // (2^(b-1) - 1)^2 for b = 4, 6, 8
+  std::vector<Upgrade> ups;
+  ups.reserve(2 * (size_t)heads);
+  for (int32_t h = 0; h < heads; ++h) {
+    const double d = decay_sq[h], r = range[h];
+    if (!(d >= 0.0 && d < 1.0)) return fail(RSQ_E_INVALID, "decay_sq[%d] must be in [0, 1)", h);
+    if (!(r >= 0.0 && std::isfinite(r))) return fail(RSQ_E_INVALID, "range[%d] must be finite and >= 0", h);
+    const double w = (r * r) / (1.0 - d);
+    for (int32_t l = 0; l < 2; ++l) {
+      const double gain = w / qsq[l] - w / qsq[l + 1];
+      if (gain > 0.0) ups.push_back({gain, h, l});
+    }
+  }
+  std::sort(ups.begin(), ups.end(), [](const Upgrade& a, const Upgrade& b) {
+    if (a.gain != b.gain) return a.gain > b.gain;
+    if (a.head != b.head) return a.head < b.head;
+    return a.level < b.level;
+  });
+  for (int32_t h = 0; h < heads; ++h) bits_out[h] = 4;
+  const long budget = ((long)std::floor((double)mean_bits * (double)heads) - 4L * heads) / 2;
+  const size_t take = std::min((size_t)budget, ups.size());
+  for (size_t u = 0; u < take; ++u) bits_out[ups[u].head] += 2;
   return RSQ_OK;
 }
 

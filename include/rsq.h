@@ -230,6 +230,25 @@ rsq_status rsq_readout(const rsq_state* st, const void* q, float* o, void* strea
 /* Synchronize `stream`, then return and clear the device status bits. */
 rsq_status rsq_get_status(rsq_state* st, uint32_t* flags, void* stream);
 
+/*
+ * Decay-aware per-head widths (host only; "Low-Bit Recurrent States in Hybrid
+ * Language Models", abstract: Gramian distortion weights and normalised state
+ * ranges). Head h at width b costs w_h / (2^(b-1) - 1)^2 with
+ * w_h = range[h]^2 / (1 - decay_sq[h]): 1 / (1 - E[a^2]) is how much of an
+ * injected error a state decaying by a_t keeps over the future steps. The
+ * widths {4, 6, 8} written to bits_out (host array [heads]) minimise the total
+ * cost with sum(bits) <= floor(mean_bits * heads); ties go to the lower head
+ * index, and a head gains width only where that lowers the cost.
+ *   decay_sq  host [heads]: E[a_t^2] of the head's decay, in [0, 1)
+ *             (GLA: the mean over key channels of E[a_t,i^2])
+ *   range     host [heads]: the head's typical group absmax (>= 0, finite)
+ *   mean_bits in [4, 8]
+ * Returns RSQ_E_INVALID on a bad argument (bits_out is then unspecified).
+ * The result can be passed as rsq_config.head_bits.
+ */
+rsq_status rsq_allocate_head_bits(const float* decay_sq, const float* range, int32_t heads,
+                                  float mean_bits, int32_t* bits_out);
+
 /* Thread-local description of the last error (never NULL). */
 const char* rsq_last_error(void);
 

@@ -14,6 +14,8 @@ Field meanings
                mixed_bits is set
   mixed_bits   None, or (n_int8_first_heads, n_int6, n_int4): per-head widths
                drawn from a seeded permutation (see head_bits_for)
+  head_bits    None, or an explicit tuple of per-head widths (overrides bits
+               and mixed_bits)
   group        scale group size along d_v
   scale_mode   'dynamic' | 'persistent' | 'yoked'
   scale_dtype  'f32' | 'f16' (storage dtype of the per-group step size)
@@ -45,6 +47,7 @@ class Workload:
     scale_mode: str
     scale_dtype: str
     mixed_bits: Optional[Tuple[int, int, int]] = None
+    head_bits: Optional[Tuple[int, ...]] = None
     trigger: float = 1.0
     bdr: bool = False
     bdr_eps: float = 0.5
@@ -69,12 +72,16 @@ class Workload:
 def head_bits_for(w: Workload) -> np.ndarray:
     """Per-head bit widths (int32 [heads]).
 
-    Uniform workloads give w.bits for every head. A mixed workload
+    An explicit w.head_bits is returned as it is. Uniform workloads give
+    w.bits for every head. A mixed workload
     (n8, n6, n4) gives INT8 to the first n8 heads and splits the remaining
     heads by a seeded permutation: the first n6 entries of
     default_rng([seed, 0]).permutation(heads - n8) become INT6, the rest INT4.
     The same assignment holds for every batch row.
     """
+    if w.head_bits is not None:
+        assert len(w.head_bits) == w.heads
+        return np.asarray(w.head_bits, dtype=np.int32)
     if w.mixed_bits is None:
         return np.full(w.heads, w.bits, dtype=np.int32)
     n8, n6, n4 = w.mixed_bits

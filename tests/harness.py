@@ -39,7 +39,7 @@ def rel_l2(a, b):
 
 def make_state(w, **over):
     import bit_recurrent_state_rsq_amd as rsq
-    hb = head_bits_for(w) if w.mixed_bits else None
+    hb = head_bits_for(w) if (w.mixed_bits or w.head_bits) else None
     kw = rsq.config_kwargs_from(w, head_bits=hb)
     kw.update(over)
     return rsq.State(**kw)
@@ -66,7 +66,7 @@ def gpu_step(st, dev_inp):
 
 
 def sub_workload(w, tiles):
-    return w.with_(batch=1, heads=len(tiles), mixed_bits=None)
+    return w.with_(batch=1, heads=len(tiles), mixed_bits=None, head_bits=None)
 
 
 def sub_inputs(inp, w, tiles):

@@ -122,6 +122,24 @@ def test_yoked_scales(model):
     assert st.get_status() & _abi.F_CLIPPED      # the scale follows the reference, codes clip
 
 
+def test_allocated_head_widths_drive_the_decode_step():
+    """Widths from rsq_allocate_head_bits (Mamba2 decays, mean 5 bits: a mix
+    of INT4, INT6 and INT8 heads) run through the decode step bit-exact."""
+    from bit_recurrent_state_rsq_amd import allocate_head_bits
+    base = CONFIGS[2]
+    w = base.with_(batch=4, heads=16, d_k=128, d_v=64, group=64, mixed_bits=None, seed=2468)
+    c = np.exp(static_params(w)["a_log"])
+    d = ((np.exp(-0.002 * c) - np.exp(-0.2 * c)) / (2 * c * 0.099)).astype(np.float32)
+    rho = np.sqrt(1.0 / (1.0 - d.astype(np.float64))).astype(np.float32)
+    rho[:2] *= 8.0                                   # two wide-range heads earn INT8
+    hb = allocate_head_bits(d, rho, 5.0)
+    log("allocated widths", hb)
+    assert {4, 6, 8} <= set(hb)
+    w = w.with_(head_bits=tuple(hb))
+    tally, st = run_parity(w, 48, check_steps=list(range(1, 9)) + [24, 47, 48])
+    tally.check()
+
+
 def test_gdn_with_d_k_256_crosses_wavefronts():
     w = CONFIGS[1].with_(batch=2, heads=2, d_k=256, d_v=64, seed=31)
     tally, st = run_parity(w, 16, check_steps=range(1, 17))
