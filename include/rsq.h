@@ -89,7 +89,8 @@ enum {
  *  persist_trigger persistent step grows when absmax > trigger * qmax * s (> 0)
  *  bdr, bdr_eps    Bounded Directional Rounding on/off; a reversed element moves
  *                  one code toward its update when the new error stays within
- *                  (0.5 + bdr_eps) * s (bdr_eps >= 0.5 corrects every reversal)
+ *                  (0.5 + bdr_eps) * s (bdr_eps >= 0.5 corrects every reversal
+ *                  whose corrected code is inside the code range)
  *  lrb_k, lrb_m    Low-Rank Bypass: k residual columns kept by a merge, a merge
  *                  every m steps (capacity k + m fp16 column pairs); m = 0 = off
  *  lrb_eps         merge threshold eps_L: |L_ij| > eps_L * s moves into the state
