@@ -25,7 +25,7 @@ from . import codec
 from .accounting import step_bytes_per_tile, workload_step_bytes
 
 __all__ = ["State", "Error", "state_bytes", "make_config", "step_bytes_per_tile",
-           "workload_step_bytes", "allocate_head_bits"]
+           "workload_step_bytes", "allocate_head_bits", "ErrorAccounting"]
 
 
 def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
@@ -187,6 +187,29 @@ class State:
             self._ptr(out, torch.float32, (B, H, dv), "o"), _stream_ptr(stream)))
         return out
 
+    def decode_step_diag(self, q, k, v, alpha, beta, acc, counts, ratio=None, out=None, stream=None):
+        """One decode step with error accounting (rsq_decode_step_diag).
+
+        acc: fp32 device tensor [tiles, 6, d_k*d_v], counts: int32 device
+        tensor [tiles, 4] (read as u32), ratio: optional fp32 [tiles, d_k*d_v].
+        Returns o_t like decode_step."""
+        torch = _torch()
+        B, H, dk, dv = self.batch, self.heads, self.d_k, self.d_v
+        idt = torch.bfloat16 if self.in_bf16 else torch.float32
+        if out is None:
+            out = torch.empty((B, H, dv), dtype=torch.float32, device=self.device)
+        ashape = (B, H, dk) if self.model == "gla" else (B, H)
+        T = B * H
+        check(lib.rsq_decode_step_diag(
+            self.h, self._ptr(q, idt, (B, H, dk), "q"), self._ptr(k, idt, (B, H, dk), "k"),
+            self._ptr(v, idt, (B, H, dv), "v"),
+            self._ptr(alpha, torch.float32, ashape, "alpha"), self._ptr(beta, torch.float32, (B, H), "beta"),
+            self._ptr(out, torch.float32, (B, H, dv), "o"),
+            self._ptr(acc, torch.float32, (T, 6, dk * dv), "acc"),
+            self._ptr(ratio, torch.float32, (T, dk * dv), "ratio"),
+            self._ptr(counts, torch.int32, (T, 4), "counts"), _stream_ptr(stream)))
+        return out
+
     def bind_step(self, q, k, v, alpha=None, beta=None, out=None, stream=None):
         """Check the step's arguments once; return a callable that issues that step.
 
@@ -343,3 +366,6 @@ class State:
                 src = torch.from_numpy(np.ascontiguousarray(data)).to(self.device)
                 host[base + off: base + off + src.numel()].copy_(src)
         torch.cuda.synchronize(self.device)
+
+
+from .diagnostics import ErrorAccounting  # noqa: E402

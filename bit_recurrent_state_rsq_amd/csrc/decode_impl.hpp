@@ -232,6 +232,9 @@ struct Decode {
   static constexpr bool kF32 = FEAT == kFeatF32;
   static constexpr bool kBypass = FEAT == kFeatBypass;
   static constexpr bool kYoked = FEAT == kFeatYoked;
+  static constexpr bool kDiag = FEAT == kFeatDiag;
+  // BDR needs the pre-rounding x next to the codes; so do the diagnostics
+  static constexpr bool kKeepX = !kF32 && (FEAT == kFeatBdr || kYoked || kDiag);
 
   struct Lds {
     float* w;      // [nwaves][WC]   per-wavefront broadcast of w (and of the reference's w)
@@ -560,12 +563,12 @@ struct Decode {
       const bool clamp = kYoked || wave_any(tiny) || (smode == kScalePersistent && a.trigger > 1.f);
 
       // requantize: t = 1.5*2^23 + 2^(b-1) + RNE(x inv)   (+ BDR toward the update's sign)
-      const bool bdr = (FEAT == kFeatBdr) || (kYoked && a.bdr);
+      const bool bdr = (FEAT == kFeatBdr) || ((kYoked || kDiag) && a.bdr);
       constexpr float lo_t = Fmt<BITS>::lo_t, hi_t = Fmt<BITS>::hi_t;
       // BDR needs x after rounding; otherwise t overwrites x in place
-      float xk[(kKeepR && (FEAT == kFeatBdr || kYoked)) ? 8 : 1][8];
-      if constexpr (kKeepR && (FEAT == kFeatBdr || kYoked)) {
-        if (bdr) {
+      float xk[kKeepX ? 8 : 1][8];
+      if constexpr (kKeepX) {
+        if (bdr || kDiag) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -587,7 +590,7 @@ struct Decode {
         }
         if (clipped) flags |= kStatusClipped;
       }
-      if constexpr (kKeepR && (FEAT == kFeatBdr || kYoked)) {
+      if constexpr (kKeepX) {
         if (bdr) {
           const float gate_k = __fadd_rn(0.5f, a.bdr_eps);
 #pragma unroll
@@ -608,11 +611,88 @@ struct Decode {
           }
         }
       }
+      if constexpr (kDiag)
+        diagnostics<BITS>(a, tile, i0, j0, t, xk, r, s_new, inv, kf, wv, dec);
       Chunk<BITS> out;
       pack_t(t, out);
       store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
       if (store_s && (lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);
+    }
+  }
+
+  // Error accounting of one step ("Preserving Updates ...", Figs. 1, 2, 4 and
+  // Table 5), per element of the lane's chunk, from the final codes:
+  //   b = fl(k_i w_j), s_hat = c s', R = fl(s_hat - x);
+  //   lost: b != 0 and c equals the code of the no-update value r on the same
+  //   grid; moved: b != 0 otherwise; reversed: b != 0 and s_hat strictly on
+  //   the far side of r from b;
+  //   E <- fl(fl(a E) + R_m), D <- fl(fl(fl(a a) D) + fl(R_m R_m)) for
+  //   m = all, lost, moved (R_m = R on the mask, 0 elsewhere);
+  //   ratio = fl(|b| RN(1/s')) for updated elements with a finite step > 0, else -1.
+  template <int BITS>
+  static __device__ __forceinline__ void diagnostics(const StepArgs& a, int tile, int i0, int j0,
+                                                     const float (&t)[8][8], const float (&xk)[8][8],
+                                                     const float (&r)[8][8], const float s_new[8],
+                                                     const float inv[8], const float kf[8], const float wv[8],
+                                                     const float dec[8]) {
+    constexpr float magic = Fmt<BITS>::magic, lo_t = Fmt<BITS>::lo_t, hi_t = Fmt<BITS>::hi_t;
+    const size_t plane = (size_t)a.dk * a.dv;
+    const size_t off = ((size_t)(j0 >> 3) * (a.dk >> 3) + (i0 >> 3)) * 64;
+    float* acc = a.dg_acc + (size_t)tile * 6 * plane + off;
+    float* rat = a.dg_ratio ? a.dg_ratio + (size_t)tile * plane + off : nullptr;
+    uint32_t n_upd = 0, n_lost = 0, n_moved = 0, n_rev = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = s_new[i];
+      const bool finite_step = s > 0.f && s <= 3.4e38f;
+      const float ai = dec[i], a2 = __fmul_rn(dec[i], dec[i]);
+      float rr[8], rl[8], rm[8], ra[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float c = t[i][j] - magic;
+        const float c0 = med3_nc(__builtin_fmaf(r[i][j], inv[i], magic), lo_t, hi_t) - magic;
+        const float b = __fmul_rn(kf[i], wv[j]);
+        const float shat = __fmul_rn(c, s);
+        const float R = __fsub_rn(shat, xk[i][j]);
+        const bool upd = b != 0.f;
+        const bool lost = upd && c == c0;
+        const bool rev = upd && s > 0.f && ((b > 0.f && shat < r[i][j]) || (b < 0.f && shat > r[i][j]));
+        n_upd += upd;
+        n_lost += lost;
+        n_moved += upd && !lost;
+        n_rev += rev;
+        rr[j] = R;
+        rl[j] = lost ? R : 0.f;
+        rm[j] = (upd && !lost) ? R : 0.f;
+        ra[j] = (upd && finite_step) ? __fmul_rn(fabsf(b), inv[i]) : -1.f;
+      }
+      const float* src[3] = {rr, rl, rm};
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        float* pe = acc + (size_t)(2 * p) * plane + 8 * i;
+        float* pd = acc + (size_t)(2 * p + 1) * plane + 8 * i;
+        float e[8], d[8];
+        loadf8(pe, e);
+        loadf8(pd, d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float Rm = src[p][j];
+          e[j] = __fadd_rn(__fmul_rn(ai, e[j]), Rm);
+          d[j] = __fadd_rn(__fmul_rn(a2, d[j]), __fmul_rn(Rm, Rm));
+        }
+        storef8(pe, e);
+        storef8(pd, d);
+      }
+      if (rat) storef8(rat + 8 * i, ra);
+    }
+    uint32_t cnt[4] = {n_upd, n_lost, n_moved, n_rev};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t v = cnt[k];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += (uint32_t)__shfl_xor((int)v, m, 64);
+      if ((threadIdx.x & 63) == 0) atomicAdd(a.dg_counts + (size_t)tile * 4 + k, v);
     }
   }
 
@@ -700,6 +780,7 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatBdr: return decode_kernel<MODEL, CL, kFeatBdr, kSpecGeneric>;
     case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass, SPEC>;
     case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
+    case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
     default: return decode_kernel<MODEL, CL, kFeatF32, kSpecGeneric>;
   }
 }

@@ -401,8 +401,19 @@ rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const vo
   return rsq_decode_step_timed(st, q, k, v, alpha, beta, o, stream, nullptr, nullptr);
 }
 
-rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
-                                 const float* beta, float* o, void* stream, void* start_event, void* stop_event) {
+}  // extern "C"
+
+namespace {
+
+struct DiagBuffers {
+  float* acc;
+  float* ratio;
+  uint32_t* counts;
+};
+
+rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
+                       const float* beta, float* o, void* stream, void* start_event, void* stop_event,
+                       const DiagBuffers* dg) {
   if (!st) return fail(RSQ_E_INVALID, "state is NULL");
   if (!q || !k || !v || !o) return fail(RSQ_E_INVALID, "q, k, v and o must be non-NULL");
   const int model = st->cfg.model;
@@ -427,6 +438,18 @@ rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, co
   else if (st->bypass) feat = rsq::kFeatBypass;
   else if (st->cfg.scale_mode == RSQ_SCALE_YOKED) feat = rsq::kFeatYoked;
   else if (st->cfg.bdr) feat = rsq::kFeatBdr;
+  if (dg) {
+    if (feat != rsq::kFeatPlain && feat != rsq::kFeatBdr)
+      return fail(RSQ_E_UNSUPPORTED, "error accounting runs on quantized states without a bypass or yoked scales");
+    if (!dg->acc || !dg->counts) return fail(RSQ_E_INVALID, "acc and counts must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(dg->acc) % 16 || reinterpret_cast<uintptr_t>(dg->ratio) % 16 ||
+        reinterpret_cast<uintptr_t>(dg->counts) % 16)
+      return fail(RSQ_E_INVALID, "accounting buffers must be 16-byte aligned");
+    feat = rsq::kFeatDiag;
+    a.dg_acc = dg->acc;
+    a.dg_ratio = dg->ratio;
+    a.dg_counts = dg->counts;
+  }
   // compile-time specialisations of (scale mode, step dtype, input dtype)
   const bool sf16 = st->cfg.scale_dtype == RSQ_F16, bf16 = st->cfg.in_dtype == RSQ_BF16;
   const int sm = st->cfg.scale_mode;
@@ -442,6 +465,22 @@ rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, co
   st->t += 1;
   if (st->bypass) st->n += 1;
   return RSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, float* o, void* stream, void* start_event, void* stop_event) {
+  return decode_step(st, q, k, v, alpha, beta, o, stream, start_event, stop_event, nullptr);
+}
+
+rsq_status rsq_decode_step_diag(rsq_state* st, const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, float* o, float* acc, float* ratio, uint32_t* counts,
+                                void* stream) {
+  const DiagBuffers dg{acc, ratio, counts};
+  return decode_step(st, q, k, v, alpha, beta, o, stream, nullptr, nullptr, &dg);
 }
 
 rsq_status rsq_merge_bypass(rsq_state* st, void* stream) {

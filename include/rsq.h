@@ -218,6 +218,34 @@ rsq_status rsq_decode_step_timed(rsq_state* st, const void* q, const void* k, co
                                  void* start_event, void* stop_event);
 
 /*
+ * rsq_decode_step with error accounting ("Preserving Updates ...", Fig. 1:
+ * per-step rounding errors R and their decayed sum E_T; Fig. 2: the coherent
+ * gain g_T and its parts on lost and moved updates; Fig. 4: lost, moved and
+ * reversed updates; Table 5: |b| / step and the lost fraction). The state
+ * advances exactly as rsq_decode_step would (same codes, steps and o). Per
+ * element of each tile, with b = fl(k_i w_j) the element's update B_t,
+ * s' the step after the scale rule, x the value before rounding, r the
+ * no-update value fl(c fl(a s)) and c the stored code:
+ *   R = fl(c s' - x); lost: b != 0 and c equals the code r rounds to on the
+ *   same grid; moved: b != 0 and not lost; reversed: b != 0 and c s' lies
+ *   strictly on the other side of r from b.
+ *   acc    device fp32 [tiles][6][d_k*d_v], each plane in the bits-32 chunk
+ *          layout of the codes (tiles b-major): E, D, E_lost, D_lost, E_moved,
+ *          D_moved, updated in place with a = the row decay of Table 1:
+ *          E <- fl(fl(a E) + R_m), D <- fl(fl(fl(a a) D) + fl(R_m R_m)),
+ *          R_m = R on the plane's mask (all, lost, moved), 0 elsewhere.
+ *          Zero it to start a window; g_T = sum E^2 / sum D.
+ *   ratio  device fp32 [tiles][d_k*d_v] (chunk layout) or NULL: this step's
+ *          fl(|b| RN(1/s')) for updated elements with a finite s' > 0, else -1
+ *   counts device u32 [tiles][4]: updated, lost, moved, reversed, added to
+ * Buffers are 16-byte aligned and owned by the caller. Returns
+ * RSQ_E_UNSUPPORTED for fp32 states, a bypass or yoked scales.
+ */
+rsq_status rsq_decode_step_diag(rsq_state* st, const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, float* o, float* acc,
+                                float* ratio, uint32_t* counts, void* stream);
+
+/*
  * Low-Rank Bypass merge: L = U W^T; elements with |L_ij| > eps_L * s move
  * into the quantized state, which is requantized (with BDR when enabled,
  * toward sign(L_ij)); the rest is replaced by a rank-k approximation kept as
