@@ -151,6 +151,88 @@ class _HipEvents:
         self.ev = []
 
 
+def accounting_report(torch, steps, batch=4, heads=4):
+    """Error accounting on synthetic inputs ("Preserving Updates ...", Figs. 1,
+    2, 4 and Table 5; the scale-state feedback of "When Dynamic Scaling
+    Fails ..."): for each Table 1 row at its workload's head shape, INT4
+    group 32 with dynamic binary16 steps, run `steps` decode steps with the
+    accounting step next to yoked-scale and fp32 states fed the same inputs,
+    once with independent steps and once with inputs that keep a persistent
+    per-tile direction (coherence 0.9). Prints one JSON line per run."""
+    import bit_recurrent_state_rsq_amd as rsq
+    from rsq_workloads import CONFIGS, static_params, step_inputs
+
+    def dev_inputs(w, inp):
+        d = {}
+        for name in ("q", "k", "v"):
+            d[name] = torch.from_numpy(np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)).cuda().view(torch.bfloat16)
+        for name in ("alpha", "beta"):
+            if name in inp:
+                d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda()
+        return d
+
+    def dense(st):
+        t = st.read_tiles()
+        if "S32" in t:
+            return t["S32"].astype(np.float64)
+        s = np.repeat(t["scales"].astype(np.float64), st.group, axis=2)
+        return t["codes"] * s
+
+    for (model, ci), rho in ((m, r) for m in (("retnet", 0), ("mamba2", 2), ("gla", 3), ("gdn", 1))
+                             for r in (0.0, 0.9)):
+        base = CONFIGS[ci]
+        w = base.with_(batch=batch, heads=heads, d_k=max(base.d_k, 128), bits=4, group=32, scale_mode="dynamic",
+                       scale_dtype="f16", in_dtype="bf16", mixed_bits=None, head_bits=None, lrb_k=0, lrb_m=0,
+                       bdr=False, seed=9000 + ci, coherence=rho)
+        kw = rsq.config_kwargs_from(w)
+        dyn = rsq.State(**kw)
+        yok = rsq.State(**dict(kw, scale_mode="yoked"))
+        f32 = rsq.State(**dict(kw, bits=32))
+        ea = rsq.ErrorAccounting(dyn)
+        sp = static_params(w)
+        norms = []
+        for t in range(1, steps + 1):
+            d = dev_inputs(w, step_inputs(w, t, sp))
+            args = (d["q"], d["k"], d["v"], d.get("alpha"), d.get("beta"))
+            if t == steps:
+                ea.counts.zero_()          # counters of the last step only
+            ea.step(*args)
+            yok.decode_step(*args)
+            f32.decode_step(*args)
+            if t in (steps // 8, steps // 4, steps // 2, steps):
+                S, Sd, Sy = dense(f32), dense(dyn), dense(yok)
+                nS = np.linalg.norm(S)
+                norms.append(dict(t=t, norm_dynamic=np.linalg.norm(Sd) / nS, norm_yoked=np.linalg.norm(Sy) / nS,
+                                  err_dynamic=np.linalg.norm(Sd - S) / nS, err_yoked=np.linalg.norm(Sy - S) / nS))
+        torch.cuda.synchronize()
+        c = ea.count_table().astype(np.int64).sum(axis=0)
+        g = ea.gains()
+        # cost of the accounting step next to the plain step, same state shape
+        d = dev_inputs(w, step_inputs(w, 1, sp))
+        args = (d["q"], d["k"], d["v"], d.get("alpha"), d.get("beta"))
+        timing = {}
+        for name, fn in (("plain", lambda: dyn.decode_step(*args)), ("accounting", lambda: ea.step(*args))):
+            for _ in range(20):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(200):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            timing[name + "_us"] = e0.elapsed_time(e1) / 200 * 1e3
+        q25, q50, q75 = ea.ratio_quartiles()
+        print(json.dumps({
+            "accounting": model, "coherence": rho, "steps": steps, "tiles": w.tiles, "d_k": w.d_k, "d_v": w.d_v,
+            "state": "int4 g32 dynamic fp16", "data": "synthetic",
+            "ratio_quartiles_last_step": [q25, q50, q75],
+            "lost_fraction_last_step": float(c[1] / max(c[0], 1)),
+            "reversed_fraction_last_step": float(c[3] / max(c[0], 1)),
+            "g_T": float(np.mean(g[:, 0])), "g_lost_T": float(np.mean(g[:, 1])), "g_moved_T": float(np.mean(g[:, 2])),
+            "state_norms": norms, "step_time": timing,
+        }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +245,8 @@ def main():
     ap.add_argument("--min-set-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-only", action="store_true",
                     help="only time a plain 1 GiB device copy (the reference for HBM counters)")
+    ap.add_argument("--accounting", type=int, default=0, metavar="T",
+                    help="instead of timing, run the error accounting for T steps per Table 1 row")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode step has no cross-GPU exchange (tiles shard "
@@ -174,6 +258,10 @@ def main():
     if args.copy_only:
         torch.cuda.set_device(0)
         print(json.dumps({"copy_reference": copy_reference(torch)}), flush=True)
+        return
+    if args.accounting:
+        torch.cuda.set_device(0)
+        accounting_report(torch, args.accounting)
         return
     import bit_recurrent_state_rsq_amd as rsq
     from rsq_workloads import CONFIGS, head_bits_for, InputPool

@@ -24,6 +24,9 @@ Field meanings
   lrb_k, lrb_m low-rank bypass: k residual columns, merge every m steps
   lrb_eps      merge threshold epsilon_L (fraction of the step size)
   gamma        RetNet decay, one value for every head
+  coherence    rho in [0, 1): k_t and v_t mix a persistent per-tile direction
+               (weight rho) with the fresh draw (weight sqrt(1 - rho^2));
+               0 = independent steps
   seed         base seed; step t draws from default_rng([seed, t]), t >= 1,
                static per-head parameters from default_rng([seed, 0])
 """
@@ -56,6 +59,7 @@ class Workload:
     lrb_eps: float = 0.5
     gamma: float = 0.97
     seed: int = 1000
+    coherence: float = 0.0
 
     @property
     def tiles(self) -> int:

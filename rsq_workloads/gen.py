@@ -46,6 +46,15 @@ def static_params(w: Workload) -> Dict[str, np.ndarray]:
         out["a_log"] = rng.uniform(0.0, 2.0, size=w.heads)  # a ~ U(0, 2)
     if w.model == "retnet":
         out["gamma"] = np.full(w.heads, w.gamma, dtype=np.float32)
+    if w.coherence > 0:
+        # per-tile persistent key and value directions, from their own stream
+        rng = np.random.default_rng([w.seed, 0, 1])
+        B, H = w.batch, w.heads
+        if w.model == "mamba2":
+            out["k_bar"] = rng.standard_normal((B, H, w.d_k)) / np.sqrt(w.d_k)
+        else:
+            out["k_bar"] = _normalized_gaussian(rng, (B, H, w.d_k))
+        out["v_bar"] = rng.standard_normal((B, H, w.d_v))
     return out
 
 
@@ -71,6 +80,16 @@ def step_inputs(w: Workload, t: int, static: Optional[Dict] = None) -> Dict[str,
         q64 = _normalized_gaussian(rng, (B, H, dk))
         k64 = _normalized_gaussian(rng, (B, H, dk))
     v64 = rng.standard_normal((B, H, dv))
+    if w.coherence > 0:
+        # mix the fresh draws with the tile's persistent directions:
+        # x = rho x_bar + sqrt(1 - rho^2) x_t (keys renormalised where the
+        # workload normalises them)
+        rho = float(w.coherence)
+        mix = np.sqrt(1.0 - rho * rho)
+        k64 = rho * static["k_bar"] + mix * k64
+        if w.model != "mamba2":
+            k64 = k64 / np.sqrt(np.sum(k64 * k64, axis=-1, keepdims=True))
+        v64 = rho * static["v_bar"] + mix * v64
     for name, x in (("q", q64), ("k", k64), ("v", v64)):
         vals, bits = _to_input(x, w.in_dtype)
         out[name] = vals
