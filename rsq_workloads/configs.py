@@ -24,6 +24,8 @@ Field meanings
   lrb_k, lrb_m low-rank bypass: k residual columns, merge every m steps
   lrb_eps      merge threshold epsilon_L (fraction of the step size)
   gamma        RetNet decay, one value for every head
+  hadamard     store the state after a Walsh-Hadamard rotation of each scale
+               group (the INT4+Had baseline); no BDR, bypass or yoked scales
   coherence    rho in [0, 1): k_t and v_t mix a persistent per-tile direction
                (weight rho) with the fresh draw (weight sqrt(1 - rho^2));
                0 = independent steps
@@ -60,6 +62,7 @@ class Workload:
     gamma: float = 0.97
     seed: int = 1000
     coherence: float = 0.0
+    hadamard: bool = False
 
     @property
     def tiles(self) -> int:
