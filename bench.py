@@ -88,7 +88,7 @@ def _oracle_worker(a):
     w, wid, ntiles, steps = a
     import oracle
     from rsq_workloads import static_params, step_inputs
-    sw = w.with_(batch=1, heads=ntiles, mixed_bits=None, seed=w.seed + 17 * wid)
+    sw = w.with_(batch=1, heads=ntiles, mixed_bits=None, head_bits=None, seed=w.seed + 17 * wid)
     static = static_params(sw)
     inps = [step_inputs(sw, t, static) for t in range(1, steps + 1)]
     st = oracle.zero_state(sw)
@@ -96,7 +96,7 @@ def _oracle_worker(a):
     st.bits = hb[np.arange(ntiles) % w.heads].astype(np.int32)
     t0 = time.perf_counter()
     for t, inp in enumerate(inps, 1):
-        st, o, d = oracle.step(st, inp, sw, oracle.F32, static)
+        st, o, d = (oracle.hadamard.step if w.hadamard else oracle.step)(st, inp, sw, oracle.F32, static)
         if w.lrb_m and t % w.lrb_m == 0:
             st, _ = oracle.merge(st, sw, oracle.F32)
     return ntiles * steps, time.perf_counter() - t0
@@ -171,12 +171,18 @@ def accounting_report(torch, steps, batch=4, heads=4):
                 d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda()
         return d
 
-    def dense(st):
+    def dense(st, rotated=False):
         t = st.read_tiles()
         if "S32" in t:
             return t["S32"].astype(np.float64)
         s = np.repeat(t["scales"].astype(np.float64), st.group, axis=2)
-        return t["codes"] * s
+        y = t["codes"] * s
+        if rotated:
+            # stored groups are y = x H (Sylvester-Hadamard): x = y H / g
+            g = st.group
+            hm = np.array([[(-1.0) ** bin(a & b).count("1") for b in range(g)] for a in range(g)])
+            y = (y.reshape(y.shape[0], y.shape[1], -1, g) @ hm / g).reshape(y.shape)
+        return y
 
     for (model, ci), rho in ((m, r) for m in (("retnet", 0), ("mamba2", 2), ("gla", 3), ("gdn", 1))
                              for r in (0.0, 0.9)):
@@ -187,6 +193,7 @@ def accounting_report(torch, steps, batch=4, heads=4):
         kw = rsq.config_kwargs_from(w)
         dyn = rsq.State(**kw)
         yok = rsq.State(**dict(kw, scale_mode="yoked"))
+        had = rsq.State(**dict(kw, hadamard=True))
         f32 = rsq.State(**dict(kw, bits=32))
         ea = rsq.ErrorAccounting(dyn)
         sp = static_params(w)
@@ -198,12 +205,15 @@ def accounting_report(torch, steps, batch=4, heads=4):
                 ea.counts.zero_()          # counters of the last step only
             ea.step(*args)
             yok.decode_step(*args)
+            had.decode_step(*args)
             f32.decode_step(*args)
             if t in (steps // 8, steps // 4, steps // 2, steps):
-                S, Sd, Sy = dense(f32), dense(dyn), dense(yok)
+                S, Sd, Sy, Sh = dense(f32), dense(dyn), dense(yok), dense(had, rotated=True)
                 nS = np.linalg.norm(S)
                 norms.append(dict(t=t, norm_dynamic=np.linalg.norm(Sd) / nS, norm_yoked=np.linalg.norm(Sy) / nS,
-                                  err_dynamic=np.linalg.norm(Sd - S) / nS, err_yoked=np.linalg.norm(Sy - S) / nS))
+                                  norm_had=np.linalg.norm(Sh) / nS,
+                                  err_dynamic=np.linalg.norm(Sd - S) / nS, err_yoked=np.linalg.norm(Sy - S) / nS,
+                                  err_had=np.linalg.norm(Sh - S) / nS))
         torch.cuda.synchronize()
         c = ea.count_table().astype(np.int64).sum(axis=0)
         g = ea.gains()
@@ -211,7 +221,8 @@ def accounting_report(torch, steps, batch=4, heads=4):
         d = dev_inputs(w, step_inputs(w, 1, sp))
         args = (d["q"], d["k"], d["v"], d.get("alpha"), d.get("beta"))
         timing = {}
-        for name, fn in (("plain", lambda: dyn.decode_step(*args)), ("accounting", lambda: ea.step(*args))):
+        for name, fn in (("plain", lambda: dyn.decode_step(*args)), ("accounting", lambda: ea.step(*args)),
+                         ("hadamard", lambda: had.decode_step(*args))):
             for _ in range(20):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,6 +256,8 @@ def main():
     ap.add_argument("--min-set-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-only", action="store_true",
                     help="only time a plain 1 GiB device copy (the reference for HBM counters)")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="store the state rotated per group (the INT4+Had baseline)")
     ap.add_argument("--accounting", type=int, default=0, metavar="T",
                     help="instead of timing, run the error accounting for T steps per Table 1 row")
     args = ap.parse_args()
@@ -267,6 +280,8 @@ def main():
     from rsq_workloads import CONFIGS, head_bits_for, InputPool
 
     w = CONFIGS[args.config]
+    if args.hadamard:
+        w = w.with_(hadamard=True)
     # the CPU baseline forks worker processes: do it before this process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(w)
     torch.cuda.set_device(0)
@@ -368,7 +383,7 @@ def main():
     value = updates / wall
     mean_ms = float(group_ms.sum() / group_n.sum())
     achieved = bytes_step / (mean_ms * 1e-3) / 1e9
-    traffic, tinfo = load_traffic(w.name, bytes_step)
+    traffic, tinfo = load_traffic(w.name + ("_had" if w.hadamard else ""), bytes_step)
     flags = [st.get_status() for st in states[: min(4, nsets)]]
 
     res = {
@@ -386,7 +401,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "model": w.model, "batch": w.batch, "heads": w.heads,
-            "d_k": w.d_k, "d_v": w.d_v, "state": "int%s" % ("/".join(str(b) for b in sorted(set(hb)))),
+            "d_k": w.d_k, "d_v": w.d_v,
+            "state": "int%s%s" % ("/".join(str(b) for b in sorted(set(hb))), "+had" if w.hadamard else ""),
             "group": w.group, "scale": "%s %s" % (w.scale_mode, w.scale_dtype), "inputs": w.in_dtype,
             "protocol": "warm (one state set)" if args.warm else "cold (%d state sets, %.2f GiB)" % (nsets, nsets * per_state / 2 ** 30),
             "parallelism": "single GPU",

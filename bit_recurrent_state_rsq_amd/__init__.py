@@ -30,7 +30,7 @@ __all__ = ["State", "Error", "state_bytes", "make_config", "step_bytes_per_tile"
 
 def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
                 scale_mode="dynamic", scale_dtype="f32", trigger=1.0, bdr=False,
-                bdr_eps=0.5, lrb_k=0, lrb_m=0, lrb_eps=0.5, gamma=None, in_dtype="f32"):
+                bdr_eps=0.5, lrb_k=0, lrb_m=0, lrb_eps=0.5, gamma=None, in_dtype="f32", hadamard=False):
     """Build an rsq_config. Returns (config, keep-alive list of host arrays)."""
     keep = []
     cfg = _abi.Config()
@@ -55,6 +55,7 @@ def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
         keep.append(g)
         cfg.gamma = ctypes.cast(g, ctypes.POINTER(ctypes.c_float))
     cfg.in_dtype = _abi.DTYPES[in_dtype] if isinstance(in_dtype, str) else int(in_dtype)
+    cfg.hadamard = int(bool(hadamard))
     return cfg, keep
 
 
@@ -69,6 +70,8 @@ def config_kwargs_from(w, head_bits=None) -> Dict:
         kw["head_bits"] = list(head_bits)
     if w.model == "retnet":
         kw["gamma"] = [w.gamma] * w.heads
+    if getattr(w, "hadamard", False):
+        kw["hadamard"] = True
     return kw
 
 

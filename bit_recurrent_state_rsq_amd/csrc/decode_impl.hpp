@@ -233,6 +233,9 @@ struct Decode {
   static constexpr bool kBypass = FEAT == kFeatBypass;
   static constexpr bool kYoked = FEAT == kFeatYoked;
   static constexpr bool kDiag = FEAT == kFeatDiag;
+  // INT4+Had: groups stored rotated; after the load phase x holds state values
+  static constexpr bool kHad = FEAT == kFeatHad;
+  static constexpr bool kDense = kF32 || kHad;
   // BDR needs the pre-rounding x next to the codes; so do the diagnostics
   static constexpr bool kKeepX = !kF32 && (FEAT == kFeatBdr || kYoked || kDiag);
 
@@ -342,6 +345,35 @@ struct Decode {
     loadf8(wrow + 8 * lc, wv);
   }
 
+  // Unnormalised Walsh-Hadamard transform of each row's scale group
+  // (INT4+Had of "Preserving Updates ...", Table 2): butterflies at column
+  // distance 1, 2, 4 inside the lane's 8 columns, then 8, 16, ... across the
+  // group's gl lanes (lane bit m = column bit 8m), each pair (a, b) at
+  // (j, j + h) becoming (fl(a + b), fl(a - b)).
+  static __device__ __forceinline__ void fwht_rows(float x[8][8], int gl, int lane) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((j & h) == 0) {
+            const float lo = x[i][j], hi = x[i][j + h];
+            x[i][j] = __fadd_rn(lo, hi);
+            x[i][j + h] = __fsub_rn(lo, hi);
+          }
+    for (int m = 1; m < gl; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = __shfl_xor(x[i][j], m, 64);
+          x[i][j] = upper ? __fsub_rn(p, x[i][j]) : __fadd_rn(x[i][j], p);
+        }
+    }
+  }
+
   static __device__ __forceinline__ float load_in1(const StepArgs& a, int tile, int j) {
     return in_elem(SP::bf16(a), a.v, (size_t)tile * a.dv + j);
   }
@@ -376,6 +408,19 @@ struct Decode {
       load_chunk<BITS>(cp, ch);
       load_scales8(sf16, sp, s_old);
       unpack_scaled(ch, x);
+      if constexpr (kHad) {
+        // the stored group is y = x H: back to x = fl(fl(c s) H) / g
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(__fmul_rn(x[i][j], invF), s_old[i]);
+        fwht_rows(x, gl, lane);
+        const float ig = 1.0f / (float)(8 * gl);   // 1/g, a power of two
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(x[i][j], ig);
+      }
     }
     float qf[8], kf[8], dec[8];
     load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
@@ -385,19 +430,19 @@ struct Decode {
     // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
     // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
     // by F = 4 (6 bits) unless the quotient is subnormal; F = 1 is no-op.
-    constexpr bool kUp = !kF32 && BITS == 4, kDown = !kF32 && BITS == 6;
+    constexpr bool kUp = !kDense && BITS == 4, kDown = !kDense && BITS == 6;
     float c1p[8], kap[8], smul[8];
     bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float c1 = kF32 ? dec[i] : __fmul_rn(dec[i], s_old[i]);
+      const float c1 = kDense ? dec[i] : __fmul_rn(dec[i], s_old[i]);
       c1p[i] = (kUp || kDown) ? __fmul_rn(c1, invF) : c1;
       if constexpr (kDown) bad = bad || subnormal(c1p[i]);
       if constexpr (kUp) {
         if (!sf16) bad = bad || !(fabsf(c1p[i]) <= 3.4e38f);
       }
-      smul[i] = kF32 ? 1.f : s_old[i];
-      if constexpr (MODEL == kGDN && !kF32) {
+      smul[i] = kDense ? 1.f : s_old[i];
+      if constexpr (MODEL == kGDN && !kDense) {
         const float ks = __fmul_rn(kf[i], s_old[i]);
         kap[i] = (kUp || kDown) ? __fmul_rn(ks, invF) : ks;
         if constexpr (kDown) bad = bad || subnormal(kap[i]);
@@ -406,7 +451,7 @@ struct Decode {
         }
       }
     }
-    const bool fast = !wave_any(bad) && (kF32 || MODEL != kGDN || (bf16 && sf16));
+    const bool fast = !wave_any(bad) && (kDense || MODEL != kGDN || (bf16 && sf16));
     if (!fast) {
       // exact long form: bring x back to the codes themselves
 #pragma unroll
@@ -420,14 +465,14 @@ struct Decode {
     // update B_t: w = v, or the delta rule
     float wv[8];
     if constexpr (MODEL == kGDN) {
-      delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kF32, wv, L.w, L.up, wrw, wr, j0,
+      delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kDense, wv, L.w, L.up, wrw, wr, j0,
                                      lane, wave);
     } else {
       load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
     }
 
     // decay and update; r = fl(c fl(a s)) kept for BDR
-    constexpr bool kKeepR = !kBypass && !kF32;
+    constexpr bool kKeepR = !kBypass && !kF32 && !kHad;
     float r[kKeepR ? 8 : 1][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -473,6 +518,8 @@ struct Decode {
       constexpr int qmax = Fmt<BITS>::qmax;
       constexpr float qmaxf = (float)qmax;
       constexpr float magic = Fmt<BITS>::magic;
+      // INT4+Had quantizes the rotated group y = x H
+      if constexpr (kHad) fwht_rows(x, gl, lane);
       // yoked reference: the same recurrence on an fp32 tile; absmax comes from it
       float xr[kYoked ? 8 : 1][8];
       if constexpr (kYoked) {
@@ -781,6 +828,7 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass, SPEC>;
     case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
     case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
+    case kFeatHad: return decode_kernel<MODEL, CL, kFeatHad, kSpecGeneric>;
     default: return decode_kernel<MODEL, CL, kFeatF32, kSpecGeneric>;
   }
 }

@@ -90,6 +90,29 @@ struct Readout {
     }
     __syncthreads();
     const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
+    if (a.hadamard) {
+      // rotated groups (INT4+Had): the row sums above are sum_i q_i (c s)_ij;
+      // o = (those sums) H / g per group, H[a][b] = (-1)^popcount(a & b)
+      float* rot = lds_z + kMaxCap * (1 + (blockDim.x >> 6));
+      for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
+        float acc = 0.f;
+        for (int q = 0; q < wrw; ++q) acc += lds_o[q * a.dv + j];
+        rot[j] = acc;
+      }
+      __syncthreads();
+      const int g = a.group;
+      const float ig = 1.0f / (float)g;
+      for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
+        const int base = j & ~(g - 1), jj = j & (g - 1);
+        float acc = 0.f;
+        for (int b = 0; b < g; ++b) {
+          const float v = rot[base + b];
+          acc += (__builtin_popcount(jj & b) & 1) ? -v : v;
+        }
+        a.o[(size_t)tile * a.dv + j] = acc * ig;
+      }
+      return;
+    }
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
       float acc = 0.f;
       for (int q = 0; q < wrw; ++q) acc += lds_o[q * a.dv + j];

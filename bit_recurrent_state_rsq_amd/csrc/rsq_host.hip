@@ -139,6 +139,9 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
     return fail(RSQ_E_UNSUPPORTED, "the low-rank bypass is not implemented for the delta rule");
   if (p.bypass && yoked) return fail(RSQ_E_UNSUPPORTED, "yoked scales with a bypass are not implemented");
   if (p.cap > rsq::kMaxCap) return fail(RSQ_E_UNSUPPORTED, "bypass capacity %d > %d", p.cap, rsq::kMaxCap);
+  if (c->hadamard != 0 && c->hadamard != 1) return fail(RSQ_E_INVALID, "hadamard %d", c->hadamard);
+  if (c->hadamard && (p.all32 || p.bypass || c->bdr || c->scale_mode == RSQ_SCALE_YOKED))
+    return fail(RSQ_E_UNSUPPORTED, "the Hadamard rotation runs on quantized states without BDR, bypass or yoked scales");
 
   // work decomposition
   Geometry& G = p.geo;
@@ -213,6 +216,7 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
                       c->bdr ? c->bdr_eps : 0.f, p.bypass ? c->lrb_eps : 0.f};
   hsh = fnv1a(hsh, fl, sizeof fl);
   if (!p.gamma.empty()) hsh = fnv1a(hsh, p.gamma.data(), p.gamma.size() * 4);
+  if (c->hadamard) hsh = fnv1a(hsh, "hadamard", 8);
   p.hash = hsh;
   return RSQ_OK;
 }
@@ -247,6 +251,7 @@ StepArgs base_args(rsq_state* st) {
   a.lrb_eps = st->cfg.lrb_eps;
   a.in_bf16 = st->cfg.in_dtype == RSQ_BF16;
   a.scale_f16 = st->cfg.scale_dtype == RSQ_F16;
+  a.hadamard = st->cfg.hadamard;
   return a;
 }
 
@@ -438,9 +443,11 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   else if (st->bypass) feat = rsq::kFeatBypass;
   else if (st->cfg.scale_mode == RSQ_SCALE_YOKED) feat = rsq::kFeatYoked;
   else if (st->cfg.bdr) feat = rsq::kFeatBdr;
+  else if (st->cfg.hadamard) feat = rsq::kFeatHad;
   if (dg) {
     if (feat != rsq::kFeatPlain && feat != rsq::kFeatBdr)
-      return fail(RSQ_E_UNSUPPORTED, "error accounting runs on quantized states without a bypass or yoked scales");
+      return fail(RSQ_E_UNSUPPORTED,
+                  "error accounting runs on quantized states without a bypass, yoked scales or a rotation");
     if (!dg->acc || !dg->counts) return fail(RSQ_E_INVALID, "acc and counts must be non-NULL");
     if (reinterpret_cast<uintptr_t>(dg->acc) % 16 || reinterpret_cast<uintptr_t>(dg->ratio) % 16 ||
         reinterpret_cast<uintptr_t>(dg->counts) % 16)

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSQ_ABI_VERSION 1
+#define RSQ_ABI_VERSION 2
 
 typedef int32_t rsq_status;
 enum {
@@ -96,6 +96,12 @@ enum {
  *  lrb_eps         merge threshold eps_L: |L_ij| > eps_L * s moves into the state
  *  gamma           RetNet only: host array [heads] of decays; NULL otherwise
  *  in_dtype        RSQ_F32 | RSQ_BF16: element type of q, k, v
+ *  hadamard        0, or 1 for the INT4+Had baseline of "Preserving Updates",
+ *                  Table 2: codes and steps describe each scale group of a
+ *                  row rotated by the g x g Sylvester-Hadamard matrix H
+ *                  (entries +-1): y = x H is what is quantized, and the state
+ *                  reads back as (c s) H / g. Quantized widths with dynamic or
+ *                  persistent scales only: no BDR, bypass or yoked scales
  *
  * Supported shapes (others return RSQ_E_UNSUPPORTED): d_v a multiple of
  * 8 * max(4, group / 8); d_k a multiple of 512 / max(4, group / 8) rows per
@@ -117,6 +123,7 @@ typedef struct rsq_config {
   float lrb_eps;
   const float* gamma;
   int32_t in_dtype;
+  int32_t hadamard;
 } rsq_config;
 
 typedef struct rsq_state rsq_state;  /* opaque host handle */

@@ -177,7 +177,8 @@ def run_parity(w, steps, check_steps, tiles=None, pool=None, st=None, merge_chec
             pre = st.read_tiles(tiles)
             ost = to_oracle(pre, w, tiles, n)
             ost.bits = tile_bits(w, tiles)
-            new, o_ref, diag = oracle.step(ost, sub_inputs(inp, w, tiles), sw, oracle.F32, ss)
+            ostep = oracle.hadamard.step if w.hadamard else oracle.step
+            new, o_ref, diag = ostep(ost, sub_inputs(inp, w, tiles), sw, oracle.F32, ss)
             o = gpu_step(st, dev)
             post = st.read_tiles(tiles)
             o_gpu = o.reshape(T, -1)[tiles].cpu().numpy()

@@ -174,3 +174,25 @@ def test_codec_roundtrips_fp32_scales_and_bypass():
         assert np.array_equal(codec.decode_scales(codec.encode_scales(s, f16), 16, 32, 8, f16), s)
     U = rng.standard_normal((2, 16, 5)).astype(np.float16).astype(np.float32)
     assert np.array_equal(codec.decode_fp16_columns(codec.encode_fp16_columns(U), 5, 16), U)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(hadamard=True, bdr=True), _abi.RSQ_E_UNSUPPORTED),
+    (dict(hadamard=True, scale_mode="yoked"), _abi.RSQ_E_UNSUPPORTED),
+    (dict(hadamard=True, bits=32), _abi.RSQ_E_UNSUPPORTED),
+    (dict(hadamard=True, model="gla", lrb_k=2, lrb_m=4), _abi.RSQ_E_UNSUPPORTED),
+])
+def test_hadamard_rejects_unsupported_combinations(change, code):
+    kw = dict(GOOD, **change)
+    st, msg = _status_of(**kw)
+    assert st == code, msg
+    assert "Hadamard" in msg
+
+
+def test_hadamard_flag_changes_the_config_identity_only_when_set():
+    ok, _ = _status_of(**dict(GOOD, hadamard=True))
+    assert ok == _abi.RSQ_OK
+    cfg, keep = make_config(**dict(GOOD, hadamard=False))
+    assert cfg.hadamard == 0
+    cfg, keep = make_config(**dict(GOOD, hadamard=True))
+    assert cfg.hadamard == 1

@@ -131,3 +131,33 @@ def test_step_matches_a_definitional_loop(model, mode):
                         got = new.codes[ti, i, G * g + jj]
                         assert got == want or diag["near"][ti, i, G * g + jj]
         st = new
+
+
+@pytest.mark.parametrize("model", ["mamba2", "gdn"])
+def test_rotation_protects_the_small_channels_of_an_outlier_group(model):
+    """What the rotation is for: with one value channel 20x larger in every
+    group, plain INT4 sets the group's step by the outlier and rounds the
+    other channels away; rotated groups spread the outlier over the group,
+    and the other channels keep well under half of plain INT4's error."""
+    base = {"gdn": CONFIGS[1], "mamba2": CONFIGS[2]}[model]
+    w = base.with_(batch=1, heads=2, d_k=16, d_v=64, group=32, bits=4, scale_mode="dynamic", scale_dtype="f16",
+                   mixed_bits=None, lrb_k=0, lrb_m=0, bdr=False, seed=5)
+    wh, wr = w.with_(hadamard=True), w.with_(bits=32)
+    sp = static_params(w)
+    a, h, r = oracle.zero_state(w), oracle.zero_state(wh), oracle.zero_state(wr)
+    ea = eh = den = 0.0
+    for t in range(1, 121):
+        inp = step_inputs(w, t, sp)
+        inp["v"] = inp["v"].copy()
+        inp["v"][..., ::32] *= 20.0
+        a, _, _ = oracle.step(a, inp, w, oracle.F64, sp)
+        h, _, _ = hd.step(h, inp, wh, oracle.F64, sp)
+        r, _, _ = oracle.step(r, inp, wr, oracle.F64, sp)
+        if t > 40:
+            S = np.asarray(r.S32, np.float64)
+            keep = np.ones(S.shape, bool)
+            keep[..., ::32] = False
+            ea += np.sum(((a.dequant() - S) ** 2)[keep])
+            eh += np.sum(((hd.dequant(h, wh, oracle.F64) - S) ** 2)[keep])
+            den += np.sum((S ** 2)[keep])
+    assert np.sqrt(eh / den) < 0.6 * np.sqrt(ea / den)
