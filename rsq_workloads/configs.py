@@ -24,6 +24,8 @@ Field meanings
   lrb_k, lrb_m low-rank bypass: k residual columns, merge every m steps
   lrb_eps      merge threshold epsilon_L (fraction of the step size)
   gamma        RetNet decay, one value for every head
+  pw_window    Gated DeltaNet only: keep the last W pure writes as FP8 pairs
+               beside the low-bit history (0 = off)
   hadamard     store the state after a Walsh-Hadamard rotation of each scale
                group (the INT4+Had baseline); no BDR, bypass or yoked scales
   coherence    rho in [0, 1): k_t and v_t mix a persistent per-tile direction
@@ -63,6 +65,7 @@ class Workload:
     seed: int = 1000
     coherence: float = 0.0
     hadamard: bool = False
+    pw_window: int = 0
 
     @property
     def tiles(self) -> int:
