@@ -30,7 +30,8 @@ __all__ = ["State", "Error", "state_bytes", "make_config", "step_bytes_per_tile"
 
 def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
                 scale_mode="dynamic", scale_dtype="f32", trigger=1.0, bdr=False,
-                bdr_eps=0.5, lrb_k=0, lrb_m=0, lrb_eps=0.5, gamma=None, in_dtype="f32", hadamard=False):
+                bdr_eps=0.5, lrb_k=0, lrb_m=0, lrb_eps=0.5, gamma=None, in_dtype="f32", hadamard=False,
+                pw_window=0):
     """Build an rsq_config. Returns (config, keep-alive list of host arrays)."""
     keep = []
     cfg = _abi.Config()
@@ -56,6 +57,7 @@ def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
         cfg.gamma = ctypes.cast(g, ctypes.POINTER(ctypes.c_float))
     cfg.in_dtype = _abi.DTYPES[in_dtype] if isinstance(in_dtype, str) else int(in_dtype)
     cfg.hadamard = int(bool(hadamard))
+    cfg.pw_window = int(pw_window)
     return cfg, keep
 
 
@@ -72,6 +74,8 @@ def config_kwargs_from(w, head_bits=None) -> Dict:
         kw["gamma"] = [w.gamma] * w.heads
     if getattr(w, "hadamard", False):
         kw["hadamard"] = True
+    if getattr(w, "pw_window", 0):
+        kw["pw_window"] = int(w.pw_window)
     return kw
 
 
@@ -142,6 +146,10 @@ class State:
         self.in_bf16 = kw.get("in_dtype", "f32") == "bf16"
         self.scale_f16 = kw.get("scale_dtype", "f32") == "f16"
         self.cap = int(kw.get("lrb_k", 0)) + int(kw.get("lrb_m", 0)) if int(kw.get("lrb_m", 0)) > 0 else 0
+        # a pure-write window keeps its W pairs in the same sections, as E4M3 bytes
+        self.pw = int(kw.get("pw_window", 0))
+        if self.pw:
+            self.cap = self.pw
         self.yoked = kw.get("scale_mode") == "yoked"
         self._sections = [self._tile_sections(hh) for hh in range(self.heads)]
 
@@ -327,7 +335,10 @@ class State:
             else:
                 codes[pos] = dec
                 scales[pos] = codec.decode_scales(raw[:, sec["scales"]:], dk, dv, g, self.scale_f16)
-            if self.cap:
+            if self.pw:
+                U[pos] = codec.decode_e4m3_columns(raw[:, sec["bypass_u"]:], self.cap, dk)
+                W[pos] = codec.decode_e4m3_columns(raw[:, sec["bypass_w"]:], self.cap, dv)
+            elif self.cap:
                 U[pos] = codec.decode_fp16_columns(raw[:, sec["bypass_u"]:], self.cap, dk)
                 W[pos] = codec.decode_fp16_columns(raw[:, sec["bypass_w"]:], self.cap, dv)
             if self.yoked:
@@ -359,10 +370,11 @@ class State:
                 parts.append((0, codec.encode_codes(codes[pos:pos + 1], sec["bits"])[0]))
             if scales is not None:
                 parts.append((sec["scales"], codec.encode_scales(scales[pos:pos + 1], self.scale_f16)[0]))
+            enc = codec.encode_e4m3_columns if self.pw else codec.encode_fp16_columns
             if U is not None:
-                parts.append((sec["bypass_u"], codec.encode_fp16_columns(U[pos:pos + 1])[0]))
+                parts.append((sec["bypass_u"], enc(U[pos:pos + 1])[0]))
             if W is not None:
-                parts.append((sec["bypass_w"], codec.encode_fp16_columns(W[pos:pos + 1])[0]))
+                parts.append((sec["bypass_w"], enc(W[pos:pos + 1])[0]))
             if ref is not None:
                 parts.append((sec["ref"], codec.encode_codes(ref[pos:pos + 1], 32)[0]))
             for off, data in parts:

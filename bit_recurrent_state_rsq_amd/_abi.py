@@ -10,7 +10,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librsq.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 RSQ_OK = 0
 RSQ_E_INVALID = -1
@@ -53,6 +53,7 @@ class Config(ctypes.Structure):
         ("gamma", ctypes.POINTER(ctypes.c_float)),
         ("in_dtype", ctypes.c_int32),
         ("hadamard", ctypes.c_int32),
+        ("pw_window", ctypes.c_int32),
     ]
 
 

@@ -92,3 +92,36 @@ def decode_fp16_columns(raw: np.ndarray, cap: int, dim: int) -> np.ndarray:
 def encode_fp16_columns(a: np.ndarray) -> np.ndarray:
     T = a.shape[0]
     return np.ascontiguousarray(a.transpose(0, 2, 1)).astype(np.float16).view(np.uint8).reshape(T, -1)
+
+
+def _e4m3_table() -> np.ndarray:
+    """float32 values of the 256 OCP E4M3 codes (bias 7, 3 mantissa bits,
+    0x7F / 0xFF NaN)."""
+    b = np.arange(256)
+    e, m = (b >> 3) & 15, b & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(b & 0x80, -mag, mag).astype(np.float32)
+
+
+E4M3 = _e4m3_table()
+
+
+def decode_e4m3_columns(raw: np.ndarray, cap: int, dim: int) -> np.ndarray:
+    """uint8 [T, cap*dim] E4M3 -> float32 [T, dim, cap] (column c contiguous in storage)."""
+    T = raw.shape[0]
+    return E4M3[raw[:, : cap * dim].astype(np.int64)].reshape(T, cap, dim).transpose(0, 2, 1).copy()
+
+
+def encode_e4m3_columns(a: np.ndarray) -> np.ndarray:
+    """float32 [T, dim, cap] of values on the E4M3 grid -> uint8 [T, cap*dim]."""
+    T = a.shape[0]
+    x = np.ascontiguousarray(a.transpose(0, 2, 1)).reshape(T, -1).astype(np.float32)
+    pos = E4M3[:127]
+    mag = np.where(np.isnan(x), 0.0, np.abs(x))
+    idx = np.searchsorted(pos, mag)
+    if np.any(pos[np.minimum(idx, 126)] != mag):
+        raise ValueError("values are not on the E4M3 grid")
+    out = (idx | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), out)
+

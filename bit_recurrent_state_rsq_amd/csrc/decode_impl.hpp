@@ -235,7 +235,9 @@ struct Decode {
   static constexpr bool kDiag = FEAT == kFeatDiag;
   // INT4+Had: groups stored rotated; after the load phase x holds state values
   static constexpr bool kHad = FEAT == kFeatHad;
-  static constexpr bool kDense = kF32 || kHad;
+  // pure-write window (Gated DeltaNet): the history takes the transition with v = 0
+  static constexpr bool kPW = FEAT == kFeatPW;
+  static constexpr bool kDense = kF32 || kHad || kPW;
   // BDR needs the pre-rounding x next to the codes; so do the diagnostics
   static constexpr bool kKeepX = !kF32 && (FEAT == kFeatBdr || kYoked || kDiag);
 
@@ -335,7 +337,7 @@ struct Decode {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int c = xtree_col<NB>(s, lane);
-      const float vj = load_in1(a, tile, j0 + c);
+      const float vj = kPW ? 0.f : load_in1(a, tile, j0 + c);
       const float w = __fmul_rn(be, __fsub_rn(vj, __fmul_rn(al, v8[s])));
       if (NB < 4 || ((lane >> 2) & 1) == 0) wrow[8 * lc + c] = w;
     }
@@ -421,6 +423,33 @@ struct Decode {
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(x[i][j], ig);
       }
+      if constexpr (kPW) {
+        // dense history fl(c s); the pair written W steps ago leaves the
+        // window and joins it before the transition: hd = fma(u_i, w_j, h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(__fmul_rn(x[i][j], invF), s_old[i]);
+        if (a.n == a.pw) {
+          const int slot = (int)((a.t_next - 1) % a.pw);
+          const uint8_t* up = tb + he.bypass_u + (size_t)slot * a.dk + i0;
+          const uint8_t* wp = tb + he.bypass_w + (size_t)slot * a.dv + j0;
+          const uint2 ub = *reinterpret_cast<const uint2*>(up);
+          const uint2 wb = *reinterpret_cast<const uint2*>(wp);
+          float ue[8], we[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ue[e] = e4m3_to_f32((ub.x >> (8 * e)) & 0xFFu);
+            ue[e + 4] = e4m3_to_f32((ub.y >> (8 * e)) & 0xFFu);
+            we[e] = e4m3_to_f32((wb.x >> (8 * e)) & 0xFFu);
+            we[e + 4] = e4m3_to_f32((wb.y >> (8 * e)) & 0xFFu);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[i][j] = __builtin_fmaf(ue[i], we[j], x[i][j]);
+        }
+      }
     }
     float qf[8], kf[8], dec[8];
     load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
@@ -472,7 +501,7 @@ struct Decode {
     }
 
     // decay and update; r = fl(c fl(a s)) kept for BDR
-    constexpr bool kKeepR = !kBypass && !kF32 && !kHad;
+    constexpr bool kKeepR = !kBypass && !kF32 && !kHad && !kPW;
     float r[kKeepR ? 8 : 1][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -496,7 +525,7 @@ struct Decode {
       }
       xtree<NB>(o8, lane);
       const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
-      if (wrw == 1 && !kBypass) {
+      if (wrw == 1 && !kBypass && !kPW) {
         // one wavefront covers every row: its sums are the readout
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
@@ -743,6 +772,88 @@ struct Decode {
     }
   }
 
+  // Pure-write window, pairs that stay ("Low-Bit GDN Recurrent-State
+  // Quantization ...", abstract: recent writes kept as FP8 pairs and carried
+  // through the full GDN transition). One wavefront per pair c:
+  //   d = cascade sum over rows (row order) of fl(k_i u_ci), b = fl(beta d),
+  //   u_ci <- e4m3(fl(alpha fl(u_ci - fl(b k_i)))),
+  // and z_c = sum_i u_ci q_i for the readout (any order). Lane l holds rows
+  // l R .. l R + R - 1 (R = d_k / 64, or one row for d_k < 64, lanes past d_k
+  // adding zeros), so the in-lane tree and then the butterfly over lanes 1, 2,
+  // ..., 32 apart give the cascade order. The new pair's z_s = sum_i e4m3(k_i) q_i.
+  static __device__ __forceinline__ void pw_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
+                                                  float* z) {
+    const int W = a.pw, n = a.n;
+    const int slot = (int)((a.t_next - 1) % W);
+    const bool leaving = n == W;
+    uint8_t* U = tb + he.bypass_u;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const bool bf16 = SP::bf16(a);
+    const float al = a.alpha[tile], be = a.beta[tile];
+    const int R = a.dk >= 64 ? a.dk >> 6 : 1;
+    for (int c = wave; c < W; c += nw) {
+      const bool is_new = c == slot;
+      const bool stays = c < n && !(leaving && c == slot);
+      if (!is_new && !stays) continue;
+      float zacc = 0.f;
+      if (is_new) {
+        for (int e = 0; e < R; ++e) {
+          const int i = lane * R + e;
+          if (i < a.dk) {
+            const float ki = in_elem(bf16, a.k, (size_t)tile * a.dk + i);
+            zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(ki)), in_elem(bf16, a.q, (size_t)tile * a.dk + i), zacc);
+          }
+        }
+      } else {
+        uint8_t* uc = U + (size_t)c * a.dk;
+        // in-lane cascade over the lane's R rows (R a power of two, at most 16)
+        float part[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = lane * R + e;
+          part[e] = (e < R && i < a.dk) ? __fmul_rn(in_elem(bf16, a.k, (size_t)tile * a.dk + i), e4m3_to_f32(uc[i]))
+                                        : 0.f;
+        }
+#pragma unroll
+        for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+          for (int e = 0; e < 16; e += 2 * h)
+            if (h < R) part[e] = __fadd_rn(part[e], part[e + h]);
+        float d = part[0];
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) d = __fadd_rn(d, __shfl_xor(d, m, 64));
+        const float b = __fmul_rn(be, d);
+        for (int e = 0; e < R; ++e) {
+          const int i = lane * R + e;
+          if (i < a.dk) {
+            const float ki = in_elem(bf16, a.k, (size_t)tile * a.dk + i);
+            const float un = __fmul_rn(al, __fsub_rn(e4m3_to_f32(uc[i]), __fmul_rn(b, ki)));
+            const uint32_t code = f32_to_e4m3(un);
+            uc[i] = (uint8_t)code;
+            zacc = __builtin_fmaf(e4m3_to_f32(code), in_elem(bf16, a.q, (size_t)tile * a.dk + i), zacc);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) zacc += __shfl_xor(zacc, m, 64);
+      if (lane == 0) z[c] = zacc;
+    }
+  }
+
+  // The new pure write (e4m3(k_t), e4m3(fl(beta_t v_t))) into slot (t - 1) mod W.
+  static __device__ __forceinline__ void pw_write_new_pair(const StepArgs& a, const HeadEntry& he, uint8_t* tb,
+                                                           int tile) {
+    const int slot = (int)((a.t_next - 1) % a.pw);
+    const bool bf16 = SP::bf16(a);
+    const float be = a.beta[tile];
+    uint8_t* U = tb + he.bypass_u + (size_t)slot * a.dk;
+    uint8_t* W = tb + he.bypass_w + (size_t)slot * a.dv;
+    for (int i = threadIdx.x; i < a.dk; i += blockDim.x)
+      U[i] = (uint8_t)f32_to_e4m3(in_elem(bf16, a.k, (size_t)tile * a.dk + i));
+    for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
+      W[j] = (uint8_t)f32_to_e4m3(__fmul_rn(be, in_elem(bf16, a.v, (size_t)tile * a.dv + j)));
+  }
+
   static __device__ void run(const StepArgs& a) {
     extern __shared__ float lds[];
     const int tile = blockIdx.x;
@@ -759,6 +870,7 @@ struct Decode {
     uint32_t flags = 0;
 
     if constexpr (kBypass) bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
+    if constexpr (kPW) pw_phase(a, he, tb, tile, L.z);
 
     if constexpr (kF32) {
       body<32>(a, he, tb, tile, L, flags);
@@ -769,7 +881,12 @@ struct Decode {
         default: body<8>(a, he, tb, tile, L, flags); break;
       }
     }
-    if (wrw > 1 || kBypass) {
+    if constexpr (kPW) {
+      // every wavefront has read the leaving pair: the new one takes its slot
+      __syncthreads();
+      pw_write_new_pair(a, he, tb, tile);
+    }
+    if (wrw > 1 || kBypass || kPW) {
       __syncthreads();
       // combine readout partials over row-wavefronts, add the bypass term, store o
       combine_o(a, he, tb, tile, L, wrw, flags);
@@ -786,6 +903,12 @@ struct Decode {
         const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
         for (int c = 0; c <= a.n; ++c) acc = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), L.z[c], acc);
       }
+      if constexpr (kPW) {
+        // window after the step: min(n + 1, W) pairs in slots 0 ..
+        const uint8_t* W = tb + he.bypass_w;
+        const int held = a.n < a.pw ? a.n + 1 : a.pw;
+        for (int c = 0; c < held; ++c) acc = __builtin_fmaf(e4m3_to_f32(W[(size_t)c * a.dv + j]), L.z[c], acc);
+      }
       if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
     }
@@ -799,7 +922,7 @@ struct Decode {
     }
     if (tile == 0 && threadIdx.x == 0) {
       *a.hdr_t = a.t_next;
-      *a.hdr_n = kBypass ? a.n + 1 : 0;
+      *a.hdr_n = kBypass ? a.n + 1 : kPW ? (a.n < a.pw ? a.n + 1 : a.pw) : 0;
     }
   }
 };
@@ -829,6 +952,9 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
     case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
     case kFeatHad: return decode_kernel<MODEL, CL, kFeatHad, kSpecGeneric>;
+    case kFeatPW:
+      if constexpr (MODEL == kGDN) return decode_kernel<MODEL, CL, kFeatPW, kSpecGeneric>;
+      else return nullptr;
     default: return decode_kernel<MODEL, CL, kFeatF32, kSpecGeneric>;
   }
 }

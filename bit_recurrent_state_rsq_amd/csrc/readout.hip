@@ -61,17 +61,25 @@ struct Readout {
     const int wrw = a.dk / WR;
     float* lds_o = lds;
     float* lds_z = lds_o + wrw * a.dv;
-    const int n = a.bypass ? a.n : 0;
+    // bypass columns (fp16) or pure-write window pairs (E4M3 bytes)
+    const bool fp8 = a.pw > 0;
+    const int n = (a.bypass || fp8) ? a.n : 0;
+    auto pair_u = [&](int c, int i) {
+      return fp8 ? e4m3_to_f32(tb[he.bypass_u + (size_t)c * a.dk + i])
+                 : __half2float(reinterpret_cast<const __half*>(tb + he.bypass_u)[(size_t)c * a.dk + i]);
+    };
+    auto pair_w = [&](int c, int j) {
+      return fp8 ? e4m3_to_f32(tb[he.bypass_w + (size_t)c * a.dv + j])
+                 : __half2float(reinterpret_cast<const __half*>(tb + he.bypass_w)[(size_t)c * a.dv + j]);
+    };
     if (n > 0) {
       // z_c = sum_i U_ic q_i
-      const __half* U = reinterpret_cast<const __half*>(tb + he.bypass_u);
       const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
       float* zpart = lds_z + kMaxCap;
       for (int c = 0; c < n; ++c) {
         float acc = 0.f;
         for (int i = threadIdx.x; i < a.dk; i += blockDim.x)
-          acc = __builtin_fmaf(__half2float(U[(size_t)c * a.dk + i]),
-                               in_elem(a.in_bf16 != 0, a.q, (size_t)tile * a.dk + i), acc);
+          acc = __builtin_fmaf(pair_u(c, i), in_elem(a.in_bf16 != 0, a.q, (size_t)tile * a.dk + i), acc);
         for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
         if (lane == 0) zpart[wave * kMaxCap + c] = acc;
       }
@@ -89,7 +97,6 @@ struct Readout {
       default: body<32>(a, he, tb, tile, lds_o); break;
     }
     __syncthreads();
-    const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
     if (a.hadamard) {
       // rotated groups (INT4+Had): the row sums above are sum_i q_i (c s)_ij;
       // o = (those sums) H / g per group, H[a][b] = (-1)^popcount(a & b)
@@ -116,7 +123,7 @@ struct Readout {
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
       float acc = 0.f;
       for (int q = 0; q < wrw; ++q) acc += lds_o[q * a.dv + j];
-      for (int c = 0; c < n; ++c) acc = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), lds_z[c], acc);
+      for (int c = 0; c < n; ++c) acc = __builtin_fmaf(pair_w(c, j), lds_z[c], acc);
       a.o[(size_t)tile * a.dv + j] = acc;
     }
   }

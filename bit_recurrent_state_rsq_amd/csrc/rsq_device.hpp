@@ -31,6 +31,28 @@ static_assert(sizeof(HeadEntry) == 32, "head table entry is 32 bytes");
 constexpr uint32_t kStatusNonfinite = 1u, kStatusScaleOverflow = 2u, kStatusClipped = 4u;
 constexpr int kMaxCap = 32;   // bypass columns a kernel can hold
 
+// OCP E4M3 (exponent bias 7, 3 mantissa bits, largest finite 448, no
+// infinities): round to nearest-even, saturate to +-448, NaN -> 0x7F with the
+// sign kept. Below 2^-6 the grid is the multiples of 2^-9 (a * 512 is exact).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return sign | 0x7Fu;
+  if (a < 0x1p-6f) return sign | (uint32_t)__builtin_rintf(a * 512.f);   // 8 is 2^-6, code 0x08
+  uint32_t r = __float_as_uint(a);
+  r = (r + 0x7FFFFu + ((r >> 20) & 1u)) & 0xFFF00000u;                    // RNE to 3 mantissa bits
+  const uint32_t e = (r >> 23) - 120u, m = (r >> 20) & 7u;                 // exponent field, bias 7
+  if (e > 15u || (e == 15u && m == 7u)) return sign | 0x7Eu;              // saturate to 448
+  return sign | (e << 3) | m;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return (c & 0x80u) ? -v : v;
+}
+
 // Round-to-nearest-even of an exact product through the float32 adder:
 // fma(x, inv, 1.5*2^23) rounds x*inv + 1.5*2^23 once, at unit spacing, so the
 // result minus the magic constant is RNE(x*inv) whenever |x*inv| < 2^22.

@@ -75,6 +75,7 @@ struct rsq_state {
   int64_t t = 0;
   int32_t n = 0;
   int32_t cap = 0;
+  int32_t pw = 0;       // pure-write window size W (0 = none)
   bool bypass = false;
   bool all32 = false;
   uint64_t hash = 0;
@@ -91,6 +92,7 @@ struct Plan {
   rsq_layout layout{};
   Geometry geo{};
   int cap = 0;
+  int pw = 0;
   bool bypass = false, all32 = false;
   uint64_t hash = 0;
 };
@@ -140,6 +142,16 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   if (p.bypass && yoked) return fail(RSQ_E_UNSUPPORTED, "yoked scales with a bypass are not implemented");
   if (p.cap > rsq::kMaxCap) return fail(RSQ_E_UNSUPPORTED, "bypass capacity %d > %d", p.cap, rsq::kMaxCap);
   if (c->hadamard != 0 && c->hadamard != 1) return fail(RSQ_E_INVALID, "hadamard %d", c->hadamard);
+  if (c->pw_window < 0 || c->pw_window > 16) return fail(RSQ_E_INVALID, "pw_window %d not in [0, 16]", c->pw_window);
+  if (c->pw_window) {
+    if (c->model != RSQ_GDN) return fail(RSQ_E_UNSUPPORTED, "the pure-write window is a Gated DeltaNet option");
+    if (p.all32 || p.bypass || c->bdr || c->hadamard || c->scale_mode == RSQ_SCALE_YOKED)
+      return fail(RSQ_E_UNSUPPORTED,
+                  "the pure-write window runs on quantized states without BDR, bypass, rotation or yoked scales");
+    if (c->d_k > 1024) return fail(RSQ_E_UNSUPPORTED, "the pure-write window needs d_k <= 1024");
+    p.pw = c->pw_window;
+    p.cap = p.pw;
+  }
   if (c->hadamard && (p.all32 || p.bypass || c->bdr || c->scale_mode == RSQ_SCALE_YOKED))
     return fail(RSQ_E_UNSUPPORTED, "the Hadamard rotation runs on quantized states without BDR, bypass or yoked scales");
 
@@ -185,7 +197,8 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
     e.head_offset = off;
     const size_t codes = (size_t)c->d_k * c->d_v * e.bits / 8;
     const size_t scales = e.bits == 32 ? 0 : (size_t)(c->d_v / g) * c->d_k * sbytes;
-    const size_t bu = (size_t)p.cap * c->d_k * 2, bw = (size_t)p.cap * c->d_v * 2;
+    const size_t pair_bytes = p.pw ? 1 : 2;   // E4M3 window pairs, fp16 bypass columns
+    const size_t bu = (size_t)p.cap * c->d_k * pair_bytes, bw = (size_t)p.cap * c->d_v * pair_bytes;
     const size_t ref = yoked ? (size_t)c->d_k * c->d_v * 4 : 0;
     size_t o = align_up(codes);
     e.scales = (uint32_t)o;
@@ -217,6 +230,7 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   hsh = fnv1a(hsh, fl, sizeof fl);
   if (!p.gamma.empty()) hsh = fnv1a(hsh, p.gamma.data(), p.gamma.size() * 4);
   if (c->hadamard) hsh = fnv1a(hsh, "hadamard", 8);
+  if (p.pw) hsh = fnv1a(hsh, &p.pw, sizeof p.pw);
   p.hash = hsh;
   return RSQ_OK;
 }
@@ -252,6 +266,7 @@ StepArgs base_args(rsq_state* st) {
   a.in_bf16 = st->cfg.in_dtype == RSQ_BF16;
   a.scale_f16 = st->cfg.scale_dtype == RSQ_F16;
   a.hadamard = st->cfg.hadamard;
+  a.pw = st->pw;
   return a;
 }
 
@@ -317,6 +332,7 @@ rsq_status rsq_state_alloc(const rsq_config* cfg, void* dev_buf, size_t buf_byte
   st->layout = p.layout;
   st->heads = p.heads;
   st->cap = p.cap;
+  st->pw = p.pw;
   st->bypass = p.bypass;
   st->all32 = p.all32;
   st->hash = p.hash;
@@ -444,6 +460,7 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   else if (st->cfg.scale_mode == RSQ_SCALE_YOKED) feat = rsq::kFeatYoked;
   else if (st->cfg.bdr) feat = rsq::kFeatBdr;
   else if (st->cfg.hadamard) feat = rsq::kFeatHad;
+  else if (st->pw) feat = rsq::kFeatPW;
   if (dg) {
     if (feat != rsq::kFeatPlain && feat != rsq::kFeatBdr)
       return fail(RSQ_E_UNSUPPORTED,
@@ -471,6 +488,7 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   if (s != RSQ_OK) return s;
   st->t += 1;
   if (st->bypass) st->n += 1;
+  if (st->pw) st->n = std::min(st->n + 1, st->pw);
   return RSQ_OK;
 }
 

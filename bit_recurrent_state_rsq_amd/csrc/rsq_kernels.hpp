@@ -8,7 +8,8 @@ namespace rsq {
 enum { kRetNet = 0, kMamba2 = 1, kGLA = 2, kGDN = 3 };
 enum { kScaleDynamic = 0, kScalePersistent = 1, kScaleYoked = 2 };
 // Compile-time feature variants of the decode kernel.
-enum { kFeatPlain = 0, kFeatBdr = 1, kFeatBypass = 2, kFeatYoked = 3, kFeatF32 = 4, kFeatDiag = 5, kFeatHad = 6 };
+enum { kFeatPlain = 0, kFeatBdr = 1, kFeatBypass = 2, kFeatYoked = 3, kFeatF32 = 4, kFeatDiag = 5, kFeatHad = 6,
+       kFeatPW = 7 };
 
 struct StepArgs {
   uint8_t* tiles;            // state buffer + tiles offset
@@ -36,6 +37,7 @@ struct StepArgs {
   int32_t in_bf16;           // q, k, v are bf16 (else fp32)
   int32_t scale_f16;         // step sizes are stored as fp16 (else fp32)
   int32_t hadamard;          // groups are stored rotated by the Sylvester-Hadamard matrix
+  int32_t pw;                // pure-write window size W (0 = none); a.n = pairs held before the step
   int64_t t_next;
   // error accounting (kFeatDiag only): per tile 6 planes of d_k*d_v floats in
   // the fp32 chunk layout, optional |b|/step per element, 4 counters

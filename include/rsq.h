@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define RSQ_ABI_VERSION 2
+#define RSQ_ABI_VERSION 3
 
 typedef int32_t rsq_status;
 enum {
@@ -102,6 +102,17 @@ enum {
  *                  (entries +-1): y = x H is what is quantized, and the state
  *                  reads back as (c s) H / g. Quantized widths with dynamic or
  *                  persistent scales only: no BDR, bypass or yoked scales
+ *  pw_window       0, or W in [1, 16]: Gated DeltaNet pure-write window
+ *                  ("Low-Bit GDN Recurrent-State Quantization: Global
+ *                  Gradient-aware Allocation and Pure-Write Sliding Windows",
+ *                  abstract). The state is the low-bit history H plus the last
+ *                  W writes as FP8 (OCP E4M3, saturating) pairs (u, w) =
+ *                  (k_t, beta_t v_t), slot (t - 1) mod W. Each step the pairs
+ *                  that stay take the transition u <- alpha (u - beta k (k^T u)),
+ *                  the pair written W steps earlier is added to H, and H takes
+ *                  the transition alone (the delta-rule step with v = 0) before
+ *                  requantization; o_t = x^T q + sum_c w_c (u_c^T q). Quantized
+ *                  widths with dynamic or persistent scales only
  *
  * Supported shapes (others return RSQ_E_UNSUPPORTED): d_v a multiple of
  * 8 * max(4, group / 8); d_k a multiple of 512 / max(4, group / 8) rows per
@@ -124,6 +135,7 @@ typedef struct rsq_config {
   const float* gamma;
   int32_t in_dtype;
   int32_t hadamard;
+  int32_t pw_window;
 } rsq_config;
 
 typedef struct rsq_state rsq_state;  /* opaque host handle */
@@ -153,7 +165,9 @@ typedef struct rsq_state rsq_state;  /* opaque host handle */
  *               bits 32: floats 8r .. 8r+7 hold columns 0..7
  *             4/6/8-bit codes are two's complement, in [-2^(b-1), 2^(b-1)-1].
  *     scales  [d_v/group][d_k] step sizes (scale_dtype); value = code * step
- *     bypass_u [k+m][d_k] fp16 (column c contiguous), bypass_w [k+m][d_v] fp16
+ *     bypass_u [k+m][d_k] fp16 (column c contiguous), bypass_w [k+m][d_v] fp16;
+ *             with a pure-write window the same sections hold u [W][d_k] and
+ *             w [W][d_v] as E4M3 bytes
  *     ref     yoked reference state, fp32, chunk layout as bits 32
  */
 typedef struct rsq_layout {

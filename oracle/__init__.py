@@ -35,9 +35,9 @@ independent pin it says "parity unpinned".
 from .fp import F32, F64, Arith, fma32, pairwise_sum, f16_round, f16_of_exact
 from .recurrence import (OState, zero_state, step, merge, readout, decay_rows,
                          scale_rule, quantize_group_codes, qrange)
-from . import closed_form, brute, accounting, allocation, diagnostics, hadamard
+from . import closed_form, brute, accounting, allocation, diagnostics, hadamard, window
 
 __all__ = ["F32", "F64", "Arith", "fma32", "pairwise_sum", "f16_round",
            "OState", "zero_state", "step", "merge", "readout", "decay_rows",
            "scale_rule", "quantize_group_codes", "qrange",
-           "closed_form", "brute", "accounting", "allocation", "diagnostics", "hadamard"]
+           "closed_form", "brute", "accounting", "allocation", "diagnostics", "hadamard", "window"]

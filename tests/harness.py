@@ -173,11 +173,13 @@ def run_parity(w, steps, check_steps, tiles=None, pool=None, st=None, merge_chec
         inp = pool.at(t) if pool is not None else step_inputs(w, t, static)
         dev = to_device(inp, w)
         if t in check_steps:
-            _, n = st.counters()
+            t_done, n = st.counters()
             pre = st.read_tiles(tiles)
             ost = to_oracle(pre, w, tiles, n)
+            ost.t = t_done
             ost.bits = tile_bits(w, tiles)
-            ostep = oracle.hadamard.step if w.hadamard else oracle.step
+            ostep = (oracle.hadamard.step if w.hadamard else oracle.window.step if w.pw_window
+                     else oracle.step)
             new, o_ref, diag = ostep(ost, sub_inputs(inp, w, tiles), sw, oracle.F32, ss)
             o = gpu_step(st, dev)
             post = st.read_tiles(tiles)

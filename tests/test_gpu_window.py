@@ -1,0 +1,87 @@
+"""GPU parity of the Gated DeltaNet pure-write window ("Low-Bit GDN
+Recurrent-State Quantization: Global Gradient-aware Allocation and Pure-Write
+Sliding Windows", abstract) against oracle/window.py, teacher-forced: history
+codes and steps bit-exact outside the decision windows, the E4M3 window pairs
+bit-exact, o_t within rel-L2 1e-4; plus the readout call, attach/restore of
+a state with a full window, and the E4M3 conversion over every input class."""
+import numpy as np
+import pytest
+
+from harness import log, make_state, rel_l2, run_parity, to_device, to_oracle
+import oracle
+from rsq_workloads import CONFIGS, static_params, step_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _w(**kw):
+    d = dict(batch=2, heads=3, d_k=128, d_v=64, group=32, bits=4, mixed_bits=None, scale_mode="persistent",
+             scale_dtype="f16", in_dtype="bf16", pw_window=8, seed=717)
+    d.update(kw)
+    return CONFIGS[1].with_(**d)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(pw_window=1),
+    dict(pw_window=3, scale_mode="dynamic"),
+    dict(pw_window=16, d_v=128),
+    dict(d_k=256, d_v=128, pw_window=5),
+    dict(bits=8, group=64, scale_dtype="f32", pw_window=4),
+    dict(bits=6, group=16, d_v=32, pw_window=2, in_dtype="f32"),
+    dict(d_k=64, group=64, d_v=64, pw_window=6),
+    dict(d_k=32, group=128, d_v=128, pw_window=7, scale_dtype="f32"),
+])
+def test_window_step_matches_oracle(kw):
+    w = _w(**kw)
+    log("pw", kw)
+    W = w.pw_window
+    steps = 2 * W + 6
+    tally, st = run_parity(w, steps, check_steps=range(1, steps + 1))
+    tally.check()
+    assert st.counters() == (steps, W)
+    assert st.get_status() == 0
+
+
+def test_window_cfg1_shape_sampled():
+    """The default workload's shape (64 x 16 tiles of 128 x 128) with W = 8,
+    sampled tiles over 64 steps."""
+    w = CONFIGS[1].with_(pw_window=8)
+    rng = np.random.default_rng(3)
+    tiles = sorted(int(b) * w.heads + h for b in rng.choice(w.batch, 2, replace=False) for h in range(w.heads))
+    tally, st = run_parity(w, 64, check_steps=list(range(1, 12)) + [31, 32, 63, 64], tiles=tiles)
+    tally.check()
+
+
+def test_window_readout_call():
+    w = _w()
+    tally, st = run_parity(w, 11, check_steps=[11])
+    arrs = st.read_tiles()
+    inp = step_inputs(w, 12, static_params(w))
+    o = st.readout(to_device(inp, w)["q"]).reshape(w.tiles, -1).cpu().numpy()
+    t, n = st.counters()
+    ost = to_oracle(arrs, w, list(range(w.tiles)), n)
+    ost.t = t
+    S = oracle.window.state_dense(ost, w)
+    q = inp["q"].reshape(w.tiles, -1).astype(np.float64)
+    assert rel_l2(o, np.einsum("ti,tij->tj", q, S)) <= 1e-5
+
+
+def test_attach_restores_a_window_state():
+    import torch
+    import bit_recurrent_state_rsq_amd as rsq
+    w = _w(pw_window=4)
+    a = make_state(w)
+    sp = static_params(w)
+    for t in range(1, 7):
+        d = to_device(step_inputs(w, t, sp), w)
+        a.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    buf = a.buf.clone()
+    b = rsq.State(buffer=buf, attach=True, **rsq.config_kwargs_from(w))
+    assert b.counters() == (6, 4)
+    d = to_device(step_inputs(w, 7, sp), w)
+    oa = a.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    ob = b.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(a.buf, b.buf)
