@@ -177,6 +177,9 @@ def accounting_report(torch, steps, batch=4, heads=4):
             return t["S32"].astype(np.float64)
         s = np.repeat(t["scales"].astype(np.float64), st.group, axis=2)
         y = t["codes"] * s
+        if st.pw:
+            n = st.counters()[1]
+            y = y + np.einsum("tic,tjc->tij", t["U"][:, :, :n].astype(np.float64), t["W"][:, :, :n].astype(np.float64))
         if rotated:
             # stored groups are y = x H (Sylvester-Hadamard): x = y H / g
             g = st.group
@@ -195,6 +198,10 @@ def accounting_report(torch, steps, batch=4, heads=4):
         yok = rsq.State(**dict(kw, scale_mode="yoked"))
         had = rsq.State(**dict(kw, hadamard=True))
         f32 = rsq.State(**dict(kw, bits=32))
+        # Gated DeltaNet: the same INT4 history with an 8-pair pure-write window, and INT6
+        extra = {}
+        if model == "gdn":
+            extra = {"pw8": rsq.State(**dict(kw, pw_window=8)), "int6": rsq.State(**dict(kw, bits=6))}
         ea = rsq.ErrorAccounting(dyn)
         sp = static_params(w)
         norms = []
@@ -207,13 +214,16 @@ def accounting_report(torch, steps, batch=4, heads=4):
             yok.decode_step(*args)
             had.decode_step(*args)
             f32.decode_step(*args)
+            for xs in extra.values():
+                xs.decode_step(*args)
             if t in (steps // 8, steps // 4, steps // 2, steps):
                 S, Sd, Sy, Sh = dense(f32), dense(dyn), dense(yok), dense(had, rotated=True)
                 nS = np.linalg.norm(S)
                 norms.append(dict(t=t, norm_dynamic=np.linalg.norm(Sd) / nS, norm_yoked=np.linalg.norm(Sy) / nS,
                                   norm_had=np.linalg.norm(Sh) / nS,
                                   err_dynamic=np.linalg.norm(Sd - S) / nS, err_yoked=np.linalg.norm(Sy - S) / nS,
-                                  err_had=np.linalg.norm(Sh - S) / nS))
+                                  err_had=np.linalg.norm(Sh - S) / nS,
+                                  **{"err_" + k: np.linalg.norm(dense(xs) - S) / nS for k, xs in extra.items()}))
         torch.cuda.synchronize()
         c = ea.count_table().astype(np.int64).sum(axis=0)
         g = ea.gains()
@@ -221,8 +231,10 @@ def accounting_report(torch, steps, batch=4, heads=4):
         d = dev_inputs(w, step_inputs(w, 1, sp))
         args = (d["q"], d["k"], d["v"], d.get("alpha"), d.get("beta"))
         timing = {}
-        for name, fn in (("plain", lambda: dyn.decode_step(*args)), ("accounting", lambda: ea.step(*args)),
-                         ("hadamard", lambda: had.decode_step(*args))):
+        runs = [("plain", lambda: dyn.decode_step(*args)), ("accounting", lambda: ea.step(*args)),
+                ("hadamard", lambda: had.decode_step(*args))]
+        runs += [(k, (lambda xs=xs: xs.decode_step(*args))) for k, xs in extra.items()]
+        for name, fn in runs:
             for _ in range(20):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -258,6 +270,8 @@ def main():
                     help="only time a plain 1 GiB device copy (the reference for HBM counters)")
     ap.add_argument("--hadamard", action="store_true",
                     help="store the state rotated per group (the INT4+Had baseline)")
+    ap.add_argument("--pw", type=int, default=0, metavar="W",
+                    help="Gated DeltaNet: keep a pure-write window of W FP8 pairs beside the history")
     ap.add_argument("--accounting", type=int, default=0, metavar="T",
                     help="instead of timing, run the error accounting for T steps per Table 1 row")
     args = ap.parse_args()
@@ -282,6 +296,8 @@ def main():
     w = CONFIGS[args.config]
     if args.hadamard:
         w = w.with_(hadamard=True)
+    if args.pw:
+        w = w.with_(pw_window=args.pw)
     # the CPU baseline forks worker processes: do it before this process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(w)
     torch.cuda.set_device(0)
@@ -378,12 +394,13 @@ def main():
     hip.destroy()
 
     bytes_step = rsq.workload_step_bytes(w.model, w.batch, hb, w.group, w.scale_dtype, w.d_k, w.d_v,
-                                         w.in_dtype, w.lrb_k, w.lrb_m)
+                                         w.in_dtype, w.lrb_k, w.lrb_m, w.pw_window)
     updates = w.batch * w.heads * K
     value = updates / wall
     mean_ms = float(group_ms.sum() / group_n.sum())
     achieved = bytes_step / (mean_ms * 1e-3) / 1e9
-    traffic, tinfo = load_traffic(w.name + ("_had" if w.hadamard else ""), bytes_step)
+    traffic, tinfo = load_traffic(w.name + ("_had" if w.hadamard else "") + ("_pw%d" % w.pw_window if w.pw_window else ""),
+                                  bytes_step)
     flags = [st.get_status() for st in states[: min(4, nsets)]]
 
     res = {
@@ -402,7 +419,8 @@ def main():
         "config": {
             "workload": w.name, "model": w.model, "batch": w.batch, "heads": w.heads,
             "d_k": w.d_k, "d_v": w.d_v,
-            "state": "int%s%s" % ("/".join(str(b) for b in sorted(set(hb))), "+had" if w.hadamard else ""),
+            "state": "int%s%s%s" % ("/".join(str(b) for b in sorted(set(hb))), "+had" if w.hadamard else "",
+                                    "+pw%d" % w.pw_window if w.pw_window else ""),
             "group": w.group, "scale": "%s %s" % (w.scale_mode, w.scale_dtype), "inputs": w.in_dtype,
             "protocol": "warm (one state set)" if args.warm else "cold (%d state sets, %.2f GiB)" % (nsets, nsets * per_state / 2 ** 30),
             "parallelism": "single GPU",

@@ -907,7 +907,12 @@ struct Decode {
         // window after the step: min(n + 1, W) pairs in slots 0 ..
         const uint8_t* W = tb + he.bypass_w;
         const int held = a.n < a.pw ? a.n + 1 : a.pw;
-        for (int c = 0; c < held; ++c) acc = __builtin_fmaf(e4m3_to_f32(W[(size_t)c * a.dv + j]), L.z[c], acc);
+        uint32_t wb[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) wb[c] = c < held ? W[(size_t)c * a.dv + j] : 0u;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (c < held) acc = __builtin_fmaf(e4m3_to_f32(wb[c]), L.z[c], acc);
       }
       if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
@@ -932,10 +937,10 @@ __global__ __launch_bounds__(512) void decode_kernel(StepArgs a) {
   Decode<MODEL, CL, FEAT, SPEC>::run(a);
 }
 
-// the specialised plain steps: at most 128 VGPRs, four wavefronts per SIMD
-template <int MODEL, int CL, int SPEC>
+// specialised steps held to at most 128 VGPRs: four wavefronts per SIMD
+template <int MODEL, int CL, int FEAT, int SPEC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel_occ(StepArgs a) {
-  Decode<MODEL, CL, kFeatPlain, SPEC>::run(a);
+  Decode<MODEL, CL, FEAT, SPEC>::run(a);
 }
 
 template <int MODEL, int CL, int SPEC>
@@ -945,7 +950,7 @@ DecodeFn decode_pick_feat(int feat) {
       // the delta-rule step with binary16 persistent steps fits 128 VGPRs without
       // spilling; the others keep their natural allocation (a spill reload waits for
       // every outstanding load, which costs more than the lost occupancy)
-      if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, SPEC>;
+      if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatPlain, SPEC>;
       else return decode_kernel<MODEL, CL, kFeatPlain, SPEC>;
     case kFeatBdr: return decode_kernel<MODEL, CL, kFeatBdr, kSpecGeneric>;
     case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass, SPEC>;
@@ -953,7 +958,8 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
     case kFeatHad: return decode_kernel<MODEL, CL, kFeatHad, kSpecGeneric>;
     case kFeatPW:
-      if constexpr (MODEL == kGDN) return decode_kernel<MODEL, CL, kFeatPW, kSpecGeneric>;
+      if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatPW, SPEC>;
+      else if constexpr (MODEL == kGDN) return decode_kernel<MODEL, CL, kFeatPW, kSpecGeneric>;
       else return nullptr;
     default: return decode_kernel<MODEL, CL, kFeatF32, kSpecGeneric>;
   }
@@ -961,7 +967,7 @@ DecodeFn decode_pick_feat(int feat) {
 
 template <int MODEL, int CL>
 DecodeFn decode_pick_spec(int feat, int spec) {
-  if (feat != kFeatPlain && feat != kFeatBypass) spec = kSpecGeneric;
+  if (feat != kFeatPlain && feat != kFeatBypass && feat != kFeatPW) spec = kSpecGeneric;
   // group-32 specialisations use 4 column lanes, group-64 ones 8
   if constexpr (CL == 4) {
     switch (spec) {

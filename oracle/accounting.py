@@ -21,15 +21,16 @@ def bits_per_element(bits, group, scale_bits, d_k, d_v, k=0, m=0):
     return avg, peak
 
 
-def tile_payload_bytes(bits, group, scale_bytes, d_k, d_v, cap=0, yoked=False):
-    """Bytes of one tile's state: codes + scales + bypass (+ fp32 reference)."""
+def tile_payload_bytes(bits, group, scale_bytes, d_k, d_v, cap=0, yoked=False, pw=0):
+    """Bytes of one tile's state: codes + scales + bypass (+ fp32 reference)
+    (+ a pure-write window of pw E4M3 pairs, one byte per value)."""
     if bits == 32:
         return 4 * d_k * d_v
     codes = d_k * d_v * bits // 8
     scales = d_k * (d_v // group) * scale_bytes
     bypass = 2 * cap * (d_k + d_v)
     ref = 4 * d_k * d_v if yoked else 0
-    return codes + scales + bypass + ref
+    return codes + scales + bypass + ref + pw * (d_k + d_v)
 
 
 def step_bytes_per_tile(bits, group, scale_bytes, d_k, d_v, in_bytes, gate_bytes,

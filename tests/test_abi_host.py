@@ -196,3 +196,43 @@ def test_hadamard_flag_changes_the_config_identity_only_when_set():
     assert cfg.hadamard == 0
     cfg, keep = make_config(**dict(GOOD, hadamard=True))
     assert cfg.hadamard == 1
+
+
+@pytest.mark.parametrize("W", [1, 8, 16])
+def test_state_bytes_with_a_pure_write_window(W):
+    """The window adds W E4M3 pairs (d_k + d_v bytes each) per tile, its two
+    sections (keys, values) each padded to 256 bytes."""
+    w = CONFIGS[1].with_(pw_window=W)
+    total = state_bytes(**config_kwargs_from(w))
+    pad = lambda n: -(-n // 256) * 256
+    payload = w.batch * w.heads * (acc.tile_payload_bytes(4, w.group, 2, w.d_k, w.d_v)
+                                   + pad(W * w.d_k) + pad(W * w.d_v))
+    if W * w.d_k % 256 == 0 and W * w.d_v % 256 == 0:
+        assert payload == w.batch * w.heads * acc.tile_payload_bytes(4, w.group, 2, w.d_k, w.d_v, pw=W)
+    table = -(-(256 + 32 * w.heads) // 256) * 256
+    assert total == table + payload
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(pw_window=17), _abi.RSQ_E_INVALID),
+    (dict(pw_window=-1), _abi.RSQ_E_INVALID),
+    (dict(pw_window=4, model="gla"), _abi.RSQ_E_UNSUPPORTED),
+    (dict(pw_window=4, bits=32), _abi.RSQ_E_UNSUPPORTED),
+    (dict(pw_window=4, bdr=True), _abi.RSQ_E_UNSUPPORTED),
+    (dict(pw_window=4, hadamard=True), _abi.RSQ_E_UNSUPPORTED),
+    (dict(pw_window=4, scale_mode="yoked"), _abi.RSQ_E_UNSUPPORTED),
+])
+def test_pure_write_window_rejects_bad_configurations(change, code):
+    st, msg = _status_of(**dict(GOOD, **change))
+    assert st == code, msg
+
+
+def test_e4m3_codec_matches_the_format():
+    """Host E4M3 table (product codec) against the oracle's, and a round trip."""
+    from oracle import window as ow
+    v = ow.e4m3_values().astype(np.float32)
+    fin = np.isfinite(v)
+    assert np.array_equal(codec.E4M3[fin], v[fin]) and np.array_equal(np.isnan(codec.E4M3), ~fin)
+    rng = np.random.default_rng(2)
+    vals = ow.fp8_round(rng.standard_normal((3, 16, 5)) * 4)
+    assert np.array_equal(codec.decode_e4m3_columns(codec.encode_e4m3_columns(vals), 5, 16), vals)
