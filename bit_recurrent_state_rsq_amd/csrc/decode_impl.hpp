@@ -196,6 +196,24 @@ __device__ __forceinline__ void div_qmax(const float m[8], float q[8]) {
   }
 }
 
+// div_qmax for two values (same arithmetic, same range check)
+template <int Q>
+__device__ __forceinline__ void div_qmax2(const float m[2], float q[2]) {
+  constexpr float qf = (float)Q, zi = 1.0f / (float)Q;
+  const float lo = min_nc(m[0], m[1]), hi = max_nc(m[0], m[1]);
+  if (wave_all(hi <= 0x1p100f && (lo >= 0x1p-100f || lo == 0.f))) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float y = __fmul_rn(m[i], zi);
+      const float r = __builtin_fmaf(-y, qf, m[i]);
+      q[i] = __builtin_fmaf(r, zi, y);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) q[i] = m[i] / qf;
+  }
+}
+
 // m / F (F a small power of two) is exact unless the quotient is subnormal
 __device__ __forceinline__ bool subnormal(float m) { return __builtin_amdgcn_class(m, 0x90) != 0; }
 
@@ -571,68 +589,149 @@ struct Decode {
       }
 
       // scale rule per row of this lane's group
+      // A group of 32 columns is a lane quad (4 lanes x 8 columns). There each
+      // lane settles two of the quad's eight rows (rows 2q, 2q+1 for quad lane
+      // q): the group maxima arrive by a reduce-scatter over the quad, the
+      // step-size arithmetic runs on two rows instead of eight, and only the
+      // reciprocals come back to every lane. Same values as the per-row form.
+      constexpr bool kSplit = SP::GL == 4;
       float s_new[8], inv[8];
+      float s2[2];                   // kSplit: steps of rows 2q, 2q+1
       bool tiny = false, grew_any = true;
-      auto row_max = [&](int i) {
-        float m = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
-        if constexpr (SP::GL > 0) return group_absmax<SP::GL>(m);
-        else return group_max_rt(m, gl);
-      };
-      if (smode == kScalePersistent) {
-        // A group grows when its absmax m exceeds thr = fl(fl(trigger qmax) s):
-        // exactly when some lane's own maximum does (thr is the same on every
-        // lane of the group), so the exchange for the group maximum is only
-        // needed on a step where some group of the wavefront grows.
-        const float trig_q = __fmul_rn(a.trigger, qmaxf);
-        float lm[8], thr[8], over[8];
+      // reciprocals of the eight rows' steps, with the zero / overflow / tiny handling
+      auto row_recips = [&]() {
+        // the common case, every step of the wavefront normal and finite, needs
+        // neither the zero / overflow handling nor the clamp
+        const float s_lo = min8(s_new), s_hi = max8(s_new);
+        const bool regular = sf16 ? (s_lo >= 0x1p-14f && s_hi <= 65504.f) : (s_lo >= 0x1p-100f && s_hi <= 0x1p100f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lm[i] = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
-          s_new[i] = s_old[i];
-          thr[i] = __fmul_rn(trig_q, s_old[i]);
-          // the sign of fl(m - thr) is the sign of m - thr
-          over[i] = __fsub_rn(lm[i], thr[i]);
+        for (int i = 0; i < 8; ++i) inv[i] = sf16 ? recip_f16val(s_new[i]) : 1.0f / s_new[i];
+        if (!wave_all(regular)) {
+          // a zero step, or an infinite one (binary16 overflow), stores code 0;
+          // tiny steps need the clamp
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (s_new[i] == 0.f || !(s_new[i] <= 3.4e38f)) inv[i] = 0.f;
+          const float imax = max8(inv);
+          if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
+          tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
         }
-        grew_any = wave_any(max8(over) > 0.f);
-        if (grew_any) {
-          // the rows that outgrew their range take fl(m / qmax) in the storage dtype
-          float m[8], ratio[8];
+      };
+      if constexpr (kSplit) {
+        const bool h2 = (lane & 2) != 0, h1 = (lane & 1) != 0;
+        float lm[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if constexpr (SP::GL > 0) m[i] = group_absmax<SP::GL>(lm[i]);
-            else m[i] = group_max_rt(lm[i], gl);
-          }
-          div_qmax<qmax>(m, ratio);
+        for (int i = 0; i < 8; ++i) lm[i] = absmax8(x[i]);
+        {
+          // reduce-scatter of the row maxima (integer max of non-negative floats,
+          // as group_absmax): first over lane q^2 (rows split 0-3 / 4-7), then q^1
+          uint32_t kp[4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float fresh = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
-            if (m[i] > thr[i]) s_new[i] = fresh;
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t mine = __float_as_uint(h2 ? lm[4 + k] : lm[k]);
+            const uint32_t other = __float_as_uint(h2 ? lm[k] : lm[4 + k]);
+            kp[k] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x4E, 0xF, 0xF, false));
           }
+          float m2[2], so[2], ratio[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t mine = h1 ? kp[2 + k] : kp[k], other = h1 ? kp[k] : kp[2 + k];
+            m2[k] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0xB1, 0xF, 0xF, false)));
+            so[k] = h2 ? (h1 ? s_old[6 + k] : s_old[4 + k]) : (h1 ? s_old[2 + k] : s_old[k]);
+          }
+          if (smode == kScalePersistent) {
+            // a group grows when its maximum exceeds fl(fl(trigger qmax) s)
+            const float trig_q = __fmul_rn(a.trigger, qmaxf);
+            bool grew[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              grew[k] = m2[k] > __fmul_rn(trig_q, so[k]);
+              s2[k] = so[k];
+            }
+            grew_any = wave_any(grew[0] || grew[1]);
+            if (grew_any) {
+              div_qmax2<qmax>(m2, ratio);
+#pragma unroll
+              for (int k = 0; k < 2; ++k)
+                if (grew[k]) s2[k] = sf16 ? __half2float(__float2half_rn(ratio[k])) : ratio[k];
+            }
+          } else {
+            div_qmax2<qmax>(m2, ratio);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) s2[k] = sf16 ? __half2float(__float2half_rn(ratio[k])) : ratio[k];
+          }
+          const float s_lo = min_nc(s2[0], s2[1]), s_hi = max_nc(s2[0], s2[1]);
+          const bool regular = sf16 ? (s_lo >= 0x1p-14f && s_hi <= 65504.f) : (s_lo >= 0x1p-100f && s_hi <= 0x1p100f);
+          float iv[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) iv[k] = sf16 ? recip_f16val(s2[k]) : 1.0f / s2[k];
+          if (!wave_all(regular)) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+              if (s2[k] == 0.f || !(s2[k] <= 3.4e38f)) iv[k] = 0.f;
+            const float imax = max_nc(iv[0], iv[1]);
+            if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
+            tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
+          }
+          // all-gather of the reciprocals: quad lane q^1, then q^2
+          float g4[4], p2[4];
+          const float p1a = dpp_xor1(iv[0]), p1b = dpp_xor1(iv[1]);
+          g4[0] = h1 ? p1a : iv[0];
+          g4[1] = h1 ? p1b : iv[1];
+          g4[2] = h1 ? iv[0] : p1a;
+          g4[3] = h1 ? iv[1] : p1b;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p2[j] = dpp_xor2(g4[j]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) inv[i] = ((i >> 2) != 0) == h2 ? g4[i & 3] : p2[i & 3];
         }
       } else {
-        // dynamic / yoked: fl(m / qmax) in the storage dtype, every row
-        float m[8], ratio[8];
+        auto row_max = [&](int i) {
+          float m = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
+          if constexpr (SP::GL > 0) return group_absmax<SP::GL>(m);
+          else return group_max_rt(m, gl);
+        };
+        if (smode == kScalePersistent) {
+          // A group grows when its absmax m exceeds thr = fl(fl(trigger qmax) s):
+          // exactly when some lane's own maximum does (thr is the same on every
+          // lane of the group), so the exchange for the group maximum is only
+          // needed on a step where some group of the wavefront grows.
+          const float trig_q = __fmul_rn(a.trigger, qmaxf);
+          float lm[8], thr[8], over[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = row_max(i);
-        div_qmax<qmax>(m, ratio);
+          for (int i = 0; i < 8; ++i) {
+            lm[i] = kYoked ? absmax8(xr[i]) : absmax8(x[i]);
+            s_new[i] = s_old[i];
+            thr[i] = __fmul_rn(trig_q, s_old[i]);
+            // the sign of fl(m - thr) is the sign of m - thr
+            over[i] = __fsub_rn(lm[i], thr[i]);
+          }
+          grew_any = wave_any(max8(over) > 0.f);
+          if (grew_any) {
+            // the rows that outgrew their range take fl(m / qmax) in the storage dtype
+            float m[8], ratio[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) s_new[i] = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
-      }
-      // the common case, every step of the wavefront normal and finite, needs
-      // neither the zero / overflow handling nor the clamp
-      const float s_lo = min8(s_new), s_hi = max8(s_new);
-      const bool regular = sf16 ? (s_lo >= 0x1p-14f && s_hi <= 65504.f) : (s_lo >= 0x1p-100f && s_hi <= 0x1p100f);
+            for (int i = 0; i < 8; ++i) {
+              if constexpr (SP::GL > 0) m[i] = group_absmax<SP::GL>(lm[i]);
+              else m[i] = group_max_rt(lm[i], gl);
+            }
+            div_qmax<qmax>(m, ratio);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) inv[i] = sf16 ? recip_f16val(s_new[i]) : 1.0f / s_new[i];
-      if (!wave_all(regular)) {
-        // a zero step, or an infinite one (binary16 overflow), stores code 0;
-        // tiny steps need the clamp
+            for (int i = 0; i < 8; ++i) {
+              const float fresh = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
+              if (m[i] > thr[i]) s_new[i] = fresh;
+            }
+          }
+        } else {
+          // dynamic / yoked: fl(m / qmax) in the storage dtype, every row
+          float m[8], ratio[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (s_new[i] == 0.f || !(s_new[i] <= 3.4e38f)) inv[i] = 0.f;
-        const float imax = max8(inv);
-        if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
-        tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
+          for (int i = 0; i < 8; ++i) m[i] = row_max(i);
+          div_qmax<qmax>(m, ratio);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s_new[i] = sf16 ? __half2float(__float2half_rn(ratio[i])) : ratio[i];
+        }
+        row_recips();
       }
       // codes can leave the range only for tiny steps, yoked scales, or a
       // persistent trigger above 1
@@ -693,7 +792,20 @@ struct Decode {
       pack_t(t, out);
       store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
-      if (store_s && (lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);
+      if constexpr (kSplit) {
+        // each quad lane stores its own two rows
+        uint8_t* sp2 = sp + (size_t)(2 * (lane & 3)) * (sf16 ? 2 : 4);
+        if (store_s) {
+          if (sf16) {
+            const uint32_t lo = __half_as_ushort(__float2half_rn(s2[0])), hi = __half_as_ushort(__float2half_rn(s2[1]));
+            *reinterpret_cast<uint32_t*>(sp2) = lo | (hi << 16);
+          } else {
+            *reinterpret_cast<float2*>(sp2) = make_float2(s2[0], s2[1]);
+          }
+        }
+      } else {
+        if (store_s && (lc & (gl - 1)) == 0) store_scales8(sf16, sp, s_new);
+      }
     }
   }
 

@@ -77,6 +77,11 @@ __device__ __forceinline__ float max_nc(float a, float b) {
   asm("v_max_f32_e32 %0, %1, %2" : "=v"(m) : "v"(a), "v"(b));
   return m;
 }
+__device__ __forceinline__ float min_nc(float a, float b) {
+  float m;
+  asm("v_min_f32_e32 %0, %1, %2" : "=v"(m) : "v"(a), "v"(b));
+  return m;
+}
 
 // max over the GL lanes of a scale group of values that are >= 0 (absolute
 // values): their bit patterns order like the values, so an integer max does
