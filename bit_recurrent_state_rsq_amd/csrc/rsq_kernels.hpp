@@ -67,54 +67,47 @@ __device__ __forceinline__ float in_elem(bool bf16, const void* p, size_t idx) {
   return reinterpret_cast<const float*>(p)[idx];
 }
 
+// Sum over the 64 lanes of a wavefront in a fixed order (every lane gets it):
+// lane pairs 1, 2, 4, 8, 16 apart by DPP / swizzle, then the two halves.
+__device__ __forceinline__ float wave_sum64(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+}
+
 // Bypass side of a decode step (Low-Rank Bypass of "Preserving Updates in
 // Low-Bit Recurrent State Quantization"; all of B_t goes to the bypass):
 //   U[:, c] <- RN16(a_i U_ic) for c < n, U[:, n] = fp16(k), W[:, n] = fp16(w),
 // and z_c = sum_i U_ic q_i (c <= n) for the readout term W z, left in lds_z.
+// Column c belongs to wavefront c mod nw, whose lanes stride over the rows:
+// the loads of a column are coalesced, and each column's sum is one wave
+// reduction (the readout that uses it is order-free).
 __device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                    float* lds_z, int model) {
+                                                    float* lds_z, int model) {
   __half* U = reinterpret_cast<__half*>(tb + he.bypass_u);
   __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
   const int n = a.n;
-  float zacc[kMaxCap];
-#pragma unroll
-  for (int c = 0; c < kMaxCap; ++c) zacc[c] = 0.f;
-  for (int i = threadIdx.x; i < a.dk; i += blockDim.x) {
-    const float ai = row_decay(a, he, model, tile, i);
-    const float qi = in_elem(a.in_bf16, a.q, (size_t)tile * a.dk + i);
-    const float ki = in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i);
-#pragma unroll
-    for (int c = 0; c < kMaxCap; ++c) {
-      if (c < n) {
-        const __half un = mul_rn_half(ai, U[(size_t)c * a.dk + i]);
-        U[(size_t)c * a.dk + i] = un;
-        zacc[c] = __builtin_fmaf(__half2float(un), qi, zacc[c]);
-      } else if (c == n) {
-        const __half un = __float2half_rn(ki);
-        U[(size_t)c * a.dk + i] = un;
-        zacc[c] = __builtin_fmaf(__half2float(un), qi, zacc[c]);
-      }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  for (int c = wave; c <= n; c += nw) {
+    __half* uc = U + (size_t)c * a.dk;
+    float acc = 0.f;
+    for (int i = lane; i < a.dk; i += 64) {
+      const float qi = in_elem(a.in_bf16, a.q, (size_t)tile * a.dk + i);
+      __half un;
+      if (c < n) un = mul_rn_half(row_decay(a, he, model, tile, i), uc[i]);
+      else un = __float2half_rn(in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i));
+      uc[i] = un;
+      acc = __builtin_fmaf(__half2float(un), qi, acc);
     }
+    acc = wave_sum64(acc);
+    if (lane == 0) lds_z[c] = acc;
   }
   for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
     W[(size_t)n * a.dv + j] = __float2half_rn(in_elem(a.in_bf16, a.v, (size_t)tile * a.dv + j));
-  // block reduction of zacc[0..n]
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  float* zpart = lds_z + kMaxCap;
-#pragma unroll
-  for (int c = 0; c < kMaxCap; ++c) {
-    if (c <= n) {
-      float v = zacc[c];
-      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-      if (lane == 0) zpart[wave * kMaxCap + c] = v;
-    }
-  }
-  __syncthreads();
-  if ((int)threadIdx.x <= n) {
-    float s = 0.f;
-    for (int w = 0; w < nw; ++w) s += zpart[w * kMaxCap + threadIdx.x];
-    lds_z[threadIdx.x] = s;
-  }
   __syncthreads();
 }
 
