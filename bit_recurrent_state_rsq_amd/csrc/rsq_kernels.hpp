@@ -95,13 +95,32 @@ __device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const Hea
   for (int c = wave; c <= n; c += nw) {
     __half* uc = U + (size_t)c * a.dk;
     float acc = 0.f;
-    for (int i = lane; i < a.dk; i += 64) {
-      const float qi = in_elem(a.in_bf16, a.q, (size_t)tile * a.dk + i);
-      __half un;
-      if (c < n) un = mul_rn_half(row_decay(a, he, model, tile, i), uc[i]);
-      else un = __float2half_rn(in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i));
-      uc[i] = un;
-      acc = __builtin_fmaf(__half2float(un), qi, acc);
+    // four rows per lane at a time, all loads issued before the stores (which
+    // could alias later loads for all the compiler knows)
+    for (int i0 = lane; i0 < a.dk; i0 += 256) {
+      float qv[4], av[4];
+      __half uv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 64 * r;
+        const bool ok = i < a.dk;
+        qv[r] = ok ? in_elem(a.in_bf16, a.q, (size_t)tile * a.dk + i) : 0.f;
+        if (c < n) {
+          av[r] = ok ? row_decay(a, he, model, tile, i) : 0.f;
+          uv[r] = ok ? uc[i] : __float2half_rn(0.f);
+        } else {
+          av[r] = ok ? in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 64 * r;
+        if (i < a.dk) {
+          const __half un = c < n ? mul_rn_half(av[r], uv[r]) : __float2half_rn(av[r]);
+          uc[i] = un;
+          acc = __builtin_fmaf(__half2float(un), qv[r], acc);
+        }
+      }
     }
     acc = wave_sum64(acc);
     if (lane == 0) lds_z[c] = acc;
