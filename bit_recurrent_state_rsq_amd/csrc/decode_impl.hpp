@@ -239,6 +239,107 @@ struct Spec {
   }
 };
 
+// Pure-write window, pairs that stay ("Low-Bit GDN Recurrent-State
+// Quantization ...", abstract: recent writes kept as FP8 pairs and carried
+// through the full GDN transition). One wavefront per pair c:
+//   d = cascade sum over rows (row order) of fl(k_i u_ci), b = fl(beta d),
+//   u_ci <- e4m3(fl(alpha fl(u_ci - fl(b k_i)))),
+// and z_c = sum_i u_ci q_i for the readout (any order). Lane l holds rows
+// l R .. l R + R - 1 (R = d_k / 64, or one row for d_k < 64, lanes past d_k
+// adding zeros), so the in-lane tree and then the butterfly over lanes 1, 2,
+// ..., 32 apart give the cascade order. The new pair's z_s = sum_i e4m3(k_i) q_i.
+static __device__ __noinline__ void pw_pairs(uint8_t* U, const void* kp, const void* qp, bool bf16, int tile, int dk, int W,
+                                           int n, int slot, float al, float be, float* z) {
+  const bool leaving = n == W;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int R = dk >= 64 ? dk >> 6 : 1;   // rows per lane: 1 .. 16, a power of two
+  // k and q of the lane's first four rows stay in registers for every pair
+  float k4[4], q4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = lane * R + e;
+    const bool ok = e < R && i < dk;
+    k4[e] = ok ? in_elem(bf16, kp, (size_t)tile * dk + i) : 0.f;
+    q4[e] = ok ? in_elem(bf16, qp, (size_t)tile * dk + i) : 0.f;
+  }
+  auto kq = [&](int e, float& ke, float& qe) {
+    const int i = lane * R + e;
+    ke = in_elem(bf16, kp, (size_t)tile * dk + i);
+    qe = in_elem(bf16, qp, (size_t)tile * dk + i);
+  };
+  for (int c = wave; c < W; c += nw) {
+    const bool is_new = c == slot;
+    const bool stays = c < n && !(leaving && c == slot);
+    if (!is_new && !stays) continue;
+    float zacc = 0.f;
+    if (is_new) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = blk * 4 + e;
+          if (r >= R || lane * R + r >= dk) continue;
+          float ke = 0.f, qe = 0.f;
+          if (blk == 0) ke = k4[e], qe = q4[e];
+          else kq(r, ke, qe);
+          zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(ke)), qe, zacc);
+        }
+    } else {
+      uint8_t* uc = U + (size_t)c * dk;
+      // in-lane cascade over the lane's R rows, in blocks of four: each block
+      // pairwise, then the block sums pairwise
+      float u4[4], bs[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        bs[blk] = 0.f;
+        if (blk * 4 >= R) continue;
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = blk * 4 + e, i = lane * R + r;
+          float ue = 0.f, ke = 0.f, qe = 0.f;
+          if (r < R && i < dk) {
+            ue = e4m3_to_f32(uc[i]);
+            if (blk == 0) ke = k4[e];
+            else kq(r, ke, qe);
+          }
+          if (blk == 0) u4[e] = ue;
+          pe[e] = __fmul_rn(ke, ue);
+        }
+        if (1 < R) { pe[0] = __fadd_rn(pe[0], pe[1]); pe[2] = __fadd_rn(pe[2], pe[3]); }
+        if (2 < R) pe[0] = __fadd_rn(pe[0], pe[2]);
+        bs[blk] = pe[0];
+      }
+      if (4 < R) { bs[0] = __fadd_rn(bs[0], bs[1]); bs[2] = __fadd_rn(bs[2], bs[3]); }
+      if (8 < R) bs[0] = __fadd_rn(bs[0], bs[2]);
+      // then over lanes 1, 2, 4, ..., 32 apart (both lanes of a pair form the same sum)
+      float d = bs[0];
+      d = __fadd_rn(d, dpp_xor1(d));
+      d = __fadd_rn(d, dpp_xor2(d));
+      d = __fadd_rn(d, swz_xor(d, 4));
+      d = __fadd_rn(d, dpp_ror8(d));
+      d = __fadd_rn(d, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(d), 0x401F)));
+      d = __fadd_rn(d, __shfl_xor(d, 32, 64));
+      const float b = __fmul_rn(be, d);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = blk * 4 + e, i = lane * R + r;
+          if (r >= R || i >= dk) continue;
+          float ue, ke, qe;
+          if (blk == 0) ue = u4[e], ke = k4[e], qe = q4[e];
+          else { ue = e4m3_to_f32(uc[i]); kq(r, ke, qe); }
+          const uint32_t code = f32_to_e4m3(__fmul_rn(al, __fsub_rn(ue, __fmul_rn(b, ke))));
+          uc[i] = (uint8_t)code;
+          zacc = __builtin_fmaf(e4m3_to_f32(code), qe, zacc);
+        }
+    }
+    zacc = wave_sum64(zacc);
+    if (lane == 0) z[c] = zacc;
+  }
+}
+
 template <int MODEL, int CL, int FEAT, int SPEC>
 struct Decode {
   using SP = Spec<SPEC>;
@@ -884,72 +985,13 @@ struct Decode {
     }
   }
 
-  // Pure-write window, pairs that stay ("Low-Bit GDN Recurrent-State
-  // Quantization ...", abstract: recent writes kept as FP8 pairs and carried
-  // through the full GDN transition). One wavefront per pair c:
-  //   d = cascade sum over rows (row order) of fl(k_i u_ci), b = fl(beta d),
-  //   u_ci <- e4m3(fl(alpha fl(u_ci - fl(b k_i)))),
-  // and z_c = sum_i u_ci q_i for the readout (any order). Lane l holds rows
-  // l R .. l R + R - 1 (R = d_k / 64, or one row for d_k < 64, lanes past d_k
-  // adding zeros), so the in-lane tree and then the butterfly over lanes 1, 2,
-  // ..., 32 apart give the cascade order. The new pair's z_s = sum_i e4m3(k_i) q_i.
+  // Pure-write window: the pairs' transitions and the readout projections
+  // (pw_pairs below), kept out of line so that its registers do not add to
+  // the body's.
   static __device__ __forceinline__ void pw_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                                   float* z) {
-    const int W = a.pw, n = a.n;
-    const int slot = (int)((a.t_next - 1) % W);
-    const bool leaving = n == W;
-    uint8_t* U = tb + he.bypass_u;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-    const bool bf16 = SP::bf16(a);
-    const float al = a.alpha[tile], be = a.beta[tile];
-    const int R = a.dk >= 64 ? a.dk >> 6 : 1;
-    for (int c = wave; c < W; c += nw) {
-      const bool is_new = c == slot;
-      const bool stays = c < n && !(leaving && c == slot);
-      if (!is_new && !stays) continue;
-      float zacc = 0.f;
-      if (is_new) {
-        for (int e = 0; e < R; ++e) {
-          const int i = lane * R + e;
-          if (i < a.dk) {
-            const float ki = in_elem(bf16, a.k, (size_t)tile * a.dk + i);
-            zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(ki)), in_elem(bf16, a.q, (size_t)tile * a.dk + i), zacc);
-          }
-        }
-      } else {
-        uint8_t* uc = U + (size_t)c * a.dk;
-        // in-lane cascade over the lane's R rows (R a power of two, at most 16)
-        float part[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int i = lane * R + e;
-          part[e] = (e < R && i < a.dk) ? __fmul_rn(in_elem(bf16, a.k, (size_t)tile * a.dk + i), e4m3_to_f32(uc[i]))
-                                        : 0.f;
-        }
-#pragma unroll
-        for (int h = 1; h < 16; h <<= 1)
-#pragma unroll
-          for (int e = 0; e < 16; e += 2 * h)
-            if (h < R) part[e] = __fadd_rn(part[e], part[e + h]);
-        float d = part[0];
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) d = __fadd_rn(d, __shfl_xor(d, m, 64));
-        const float b = __fmul_rn(be, d);
-        for (int e = 0; e < R; ++e) {
-          const int i = lane * R + e;
-          if (i < a.dk) {
-            const float ki = in_elem(bf16, a.k, (size_t)tile * a.dk + i);
-            const float un = __fmul_rn(al, __fsub_rn(e4m3_to_f32(uc[i]), __fmul_rn(b, ki)));
-            const uint32_t code = f32_to_e4m3(un);
-            uc[i] = (uint8_t)code;
-            zacc = __builtin_fmaf(e4m3_to_f32(code), in_elem(bf16, a.q, (size_t)tile * a.dk + i), zacc);
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) zacc += __shfl_xor(zacc, m, 64);
-      if (lane == 0) z[c] = zacc;
-    }
+    pw_pairs(tb + he.bypass_u, a.k, a.q, SP::bf16(a), tile, a.dk, a.pw, a.n, (int)((a.t_next - 1) % a.pw),
+             a.alpha[tile], a.beta[tile], z);
   }
 
   // The new pure write (e4m3(k_t), e4m3(fl(beta_t v_t))) into slot (t - 1) mod W.
@@ -1008,28 +1050,42 @@ struct Decode {
 
   static __device__ __forceinline__ void combine_o(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
                                                    int tile, const Lds& L, int wrw, uint32_t& flags) {
+    // bypass columns (fp16) / window pairs (E4M3): cnt columns of W, each
+    // weighted by its z. The sum W z is spread over every thread of the
+    // block: thread (p, j) takes columns p, p + P, ... of row j of W (its
+    // loads in flight together), the P partials meet in LDS (L.up, free here:
+    // P d_v <= 2 wrw d_v floats).
+    constexpr bool kWz = kBypass || kPW;
+    const int cnt = kBypass ? a.n + 1 : kPW ? (a.n < a.pw ? a.n + 1 : a.pw) : 0;
+    const int P = kWz ? (int)(blockDim.x / a.dv) : 0;
+    auto wval = [&](int c, int j) {
+      if constexpr (kPW) return e4m3_to_f32(tb[he.bypass_w + (size_t)c * a.dv + j]);
+      else return __half2float(reinterpret_cast<const __half*>(tb + he.bypass_w)[(size_t)c * a.dv + j]);
+    };
+    if (kWz && P >= 1) {
+      const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
+      if (pp < P) {
+        float part = 0.f;
+        for (int c = pp; c < cnt; c += P) part = __builtin_fmaf(wval(c, j), L.z[c], part);
+        L.up[pp * a.dv + j] = part;
+      }
+      __syncthreads();
+    }
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
       float acc = L.op[j];
       for (int q = 1; q < wrw; ++q) acc += L.op[q * a.dv + j];
-      if constexpr (kBypass) {
-        const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
-        for (int c = 0; c <= a.n; ++c) acc = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), L.z[c], acc);
-      }
-      if constexpr (kPW) {
-        // window after the step: min(n + 1, W) pairs in slots 0 ..
-        const uint8_t* W = tb + he.bypass_w;
-        const int held = a.n < a.pw ? a.n + 1 : a.pw;
-        uint32_t wb[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) wb[c] = c < held ? W[(size_t)c * a.dv + j] : 0u;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (c < held) acc = __builtin_fmaf(e4m3_to_f32(wb[c]), L.z[c], acc);
+      if (kWz) {
+        if (P >= 1) {
+          for (int pp = 0; pp < P; ++pp) acc += L.up[pp * a.dv + j];
+        } else {
+          for (int c = 0; c < cnt; ++c) acc = __builtin_fmaf(wval(c, j), L.z[c], acc);
+        }
       }
       if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
     }
   }
+
 
   static __device__ __forceinline__ void finish(const StepArgs& a, int tile, uint32_t flags) {
     if (wave_any(flags != 0)) {
