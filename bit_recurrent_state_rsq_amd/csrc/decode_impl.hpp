@@ -483,14 +483,20 @@ struct Decode {
             x[i][j] = __fadd_rn(lo, hi);
             x[i][j + h] = __fsub_rn(lo, hi);
           }
-    for (int m = 1; m < gl; m <<= 1) {
-      const bool upper = (lane & m) != 0;
+    // across lanes: the partner's value p arrives by DPP / swizzle, and
+    // fma(sign, x, p) forms fl(x + p) on the lower lane, fl(p - x) on the upper
+#pragma unroll
+    for (int lvl = 0; lvl < 4; ++lvl) {
+      const int m = 1 << lvl;
+      if (m >= gl) break;
+      const float sg = (lane & m) ? -1.f : 1.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = __shfl_xor(x[i][j], m, 64);
-          x[i][j] = upper ? __fsub_rn(p, x[i][j]) : __fadd_rn(x[i][j], p);
+          const float v = x[i][j];
+          const float p = lvl == 0 ? dpp_xor1(v) : lvl == 1 ? dpp_xor2(v) : lvl == 2 ? swz_xor(v, 4) : dpp_ror8(v);
+          x[i][j] = __builtin_fmaf(sg, v, p);
         }
     }
   }
@@ -1124,7 +1130,9 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatBypass: return decode_kernel<MODEL, CL, kFeatBypass, SPEC>;
     case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
     case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
-    case kFeatHad: return decode_kernel<MODEL, CL, kFeatHad, kSpecGeneric>;
+    case kFeatHad:
+      if constexpr (SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatHad, SPEC>;
+      else return decode_kernel<MODEL, CL, kFeatHad, SPEC>;
     case kFeatPW:
       if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatPW, SPEC>;
       else if constexpr (MODEL == kGDN) return decode_kernel<MODEL, CL, kFeatPW, kSpecGeneric>;
@@ -1135,7 +1143,7 @@ DecodeFn decode_pick_feat(int feat) {
 
 template <int MODEL, int CL>
 DecodeFn decode_pick_spec(int feat, int spec) {
-  if (feat != kFeatPlain && feat != kFeatBypass && feat != kFeatPW) spec = kSpecGeneric;
+  if (feat != kFeatPlain && feat != kFeatBypass && feat != kFeatPW && feat != kFeatHad) spec = kSpecGeneric;
   // group-32 specialisations use 4 column lanes, group-64 ones 8
   if constexpr (CL == 4) {
     switch (spec) {
