@@ -702,8 +702,11 @@ struct Decode {
       // step-size arithmetic runs on two rows instead of eight, and only the
       // reciprocals come back to every lane. Same values as the per-row form.
       constexpr bool kSplit = SP::GL == 4;
+      // A group of 64 columns is 8 lanes: there each lane settles one row
+      // (row q for group lane q), the same way.
+      constexpr bool kSplit8 = SP::GL == 8 && !kYoked;
       float s_new[8], inv[8];
-      float s2[2];                   // kSplit: steps of rows 2q, 2q+1
+      float s2[2];                   // kSplit: steps of rows 2q, 2q+1; kSplit8: s2[0], row q
       bool tiny = false, grew_any = true;
       // reciprocals of the eight rows' steps, with the zero / overflow / tiny handling
       auto row_recips = [&]() {
@@ -791,6 +794,74 @@ struct Decode {
           for (int j = 0; j < 4; ++j) p2[j] = dpp_xor2(g4[j]);
 #pragma unroll
           for (int i = 0; i < 8; ++i) inv[i] = ((i >> 2) != 0) == h2 ? g4[i & 3] : p2[i & 3];
+        }
+      } else if constexpr (kSplit8) {
+        const int q = lane & 7;
+        const bool h4 = (q & 4) != 0, h2 = (q & 2) != 0, h1 = (q & 1) != 0;
+        float lm[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lm[i] = absmax8(x[i]);
+        // reduce-scatter of the row maxima over the 8 lanes (integer max of
+        // non-negative floats): halves across the half-row mirror (lane q and
+        // 7 - q), then quads (q^2), then pairs (q^1); lane q ends with row q
+        uint32_t k4[4], k2[2];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t mine = __float_as_uint(h4 ? lm[4 + r] : lm[r]);
+          const uint32_t other = __float_as_uint(h4 ? lm[r] : lm[4 + r]);
+          k4[r] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x141, 0xF, 0xF, false));
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const uint32_t mine = h2 ? k4[2 + r] : k4[r], other = h2 ? k4[r] : k4[2 + r];
+          k2[r] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x4E, 0xF, 0xF, false));
+        }
+        float m1[2], so1, ratio[2];
+        {
+          const uint32_t mine = h1 ? k2[1] : k2[0], other = h1 ? k2[0] : k2[1];
+          m1[0] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0xB1, 0xF, 0xF, false)));
+          m1[1] = m1[0];
+          const float a4 = h4 ? s_old[4] : s_old[0], b4 = h4 ? s_old[5] : s_old[1];
+          const float c4 = h4 ? s_old[6] : s_old[2], d4 = h4 ? s_old[7] : s_old[3];
+          const float lo2 = h2 ? c4 : a4, hi2 = h2 ? d4 : b4;
+          so1 = h1 ? hi2 : lo2;
+        }
+        if (smode == kScalePersistent) {
+          const float trig_q = __fmul_rn(a.trigger, qmaxf);
+          const bool grew = m1[0] > __fmul_rn(trig_q, so1);
+          s2[0] = so1;
+          grew_any = wave_any(grew);
+          if (grew_any) {
+            div_qmax2<qmax>(m1, ratio);
+            if (grew) s2[0] = sf16 ? __half2float(__float2half_rn(ratio[0])) : ratio[0];
+          }
+        } else {
+          div_qmax2<qmax>(m1, ratio);
+          s2[0] = sf16 ? __half2float(__float2half_rn(ratio[0])) : ratio[0];
+        }
+        const float sv = s2[0];
+        const bool regular = sf16 ? (sv >= 0x1p-14f && sv <= 65504.f) : (sv >= 0x1p-100f && sv <= 0x1p100f);
+        float iv = sf16 ? recip_f16val(sv) : 1.0f / sv;
+        if (!wave_all(regular)) {
+          if (sv == 0.f || !(sv <= 3.4e38f)) iv = 0.f;
+          if (!(sv <= 3.4e38f)) flags |= kStatusScaleOverflow;
+          tiny = !(sv <= 3.4e38f) || !(iv <= (sf16 ? 16384.f : 0x1p100f));
+        }
+        // all-gather of the reciprocals: pairs, quads, then halves (by q^4 via swizzle)
+        float g2[2], g4v[4];
+        const float p1 = dpp_xor1(iv);
+        g2[0] = h1 ? p1 : iv;
+        g2[1] = h1 ? iv : p1;
+        const float p2a = dpp_xor2(g2[0]), p2b = dpp_xor2(g2[1]);
+        g4v[0] = h2 ? p2a : g2[0];
+        g4v[1] = h2 ? p2b : g2[1];
+        g4v[2] = h2 ? g2[0] : p2a;
+        g4v[3] = h2 ? g2[1] : p2b;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = swz_xor(g4v[r], 4);
+          inv[r] = h4 ? pr : g4v[r];
+          inv[4 + r] = h4 ? g4v[r] : pr;
         }
       } else {
         auto row_max = [&](int i) {
@@ -899,7 +970,14 @@ struct Decode {
       pack_t(t, out);
       store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
-      if constexpr (kSplit) {
+      if constexpr (kSplit8) {
+        // each group lane stores its own row
+        if (store_s) {
+          uint8_t* sp1 = sp + (size_t)(lane & 7) * (sf16 ? 2 : 4);
+          if (sf16) *reinterpret_cast<uint16_t*>(sp1) = __half_as_ushort(__float2half_rn(s2[0]));
+          else *reinterpret_cast<float*>(sp1) = s2[0];
+        }
+      } else if constexpr (kSplit) {
         // each quad lane stores its own two rows
         uint8_t* sp2 = sp + (size_t)(2 * (lane & 3)) * (sf16 ? 2 : 4);
         if (store_s) {
