@@ -333,3 +333,39 @@ def test_merge_variants(model, bits, g, mode, sdt, dk, dv, k, m, bdr):
     tally, st = run_parity(w, steps, check_steps=range(1, steps + 1), merge_check=_merge_checker(w, merges))
     tally.check()
     assert len(merges) == 3
+
+
+def test_decode_steps_replay_from_a_hip_graph():
+    """Eight decode steps captured once in a graph (torch.cuda.CUDAGraph over
+    the caller's stream) and replayed three times give the same codes, step
+    sizes and outputs as 24 eager steps. The host-side step counter advances
+    only at capture, so this holds for states whose arithmetic does not read
+    it (no bypass, no window)."""
+    import torch
+    w = CONFIGS[1].with_(batch=4)
+    sp = static_params(w)
+    pool = [to_device(step_inputs(w, t, sp), w) for t in range(1, 9)]
+    eager, graphed = make_state(w), make_state(w)
+    outs_e = []
+    for rep in range(3):
+        for d in pool:
+            outs_e.append(gpu_step(eager, d).clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = [torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda") for _ in pool]
+    issues = [graphed.bind_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=o, stream=side)
+              for d, o in zip(pool, outs)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for issue in issues:
+            issue()
+    torch.cuda.synchronize()
+    # capture recorded the launches without running them
+    assert not graphed.read_tiles()["codes"].any()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(8):
+            assert torch.equal(outs[s], outs_e[8 * rep + s]), "replay %d step %d" % (rep, s)
+    a, b = eager.read_tiles(), graphed.read_tiles()
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
