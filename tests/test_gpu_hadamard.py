@@ -51,3 +51,16 @@ def test_hadamard_readout_call():
     q = inp["q"].reshape(w.tiles, -1).astype(np.float64)
     o_ref = np.einsum("ti,tij->tj", q, S)
     assert rel_l2(o, o_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("ci", [1, 4])
+def test_hadamard_at_the_workload_shapes_sampled(ci):
+    """The default workload (64 x 16 tiles of 128 x 128) and the mixed-width
+    one (512 x 32 tiles, INT8/INT6/INT4 heads) with rotated groups: sampled
+    tiles covering every head, checked at a spread of steps."""
+    w = CONFIGS[ci].with_(hadamard=True)
+    rng = np.random.default_rng([ci, 5])
+    rows = rng.choice(w.batch, size=2, replace=False)
+    tiles = sorted(int(b) * w.heads + h for b in rows for h in range(w.heads))
+    tally, st = run_parity(w, 48, check_steps=[1, 2, 3, 16, 47, 48], tiles=tiles)
+    tally.check()
