@@ -56,7 +56,7 @@ struct Readout {
     extern __shared__ float lds[];
     const int tile = blockIdx.x;
     const int bb = tile / a.H, h = tile - bb * a.H;
-    const HeadEntry he = a.heads[h];
+    const HeadEntry he = head_entry(a, h);
     const uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
     const int wrw = a.dk / WR;
     float* lds_o = lds;

@@ -76,6 +76,7 @@ struct rsq_state {
   int32_t n = 0;
   int32_t cap = 0;
   int32_t pw = 0;       // pure-write window size W (0 = none)
+  bool uniform = false; // every head's table entry alike up to its offset
   bool bypass = false;
   bool all32 = false;
   uint64_t hash = 0;
@@ -267,6 +268,11 @@ StepArgs base_args(rsq_state* st) {
   a.scale_f16 = st->cfg.scale_dtype == RSQ_F16;
   a.hadamard = st->cfg.hadamard;
   a.pw = st->pw;
+  a.uniform = st->uniform ? 1 : 0;
+  if (st->uniform) {
+    a.uni = st->heads[0];
+    a.uni_stride = st->heads.size() > 1 ? st->heads[1].head_offset : 0;
+  }
   return a;
 }
 
@@ -334,6 +340,14 @@ rsq_status rsq_state_alloc(const rsq_config* cfg, void* dev_buf, size_t buf_byte
   st->cap = p.cap;
   st->pw = p.pw;
   st->bypass = p.bypass;
+  st->uniform = true;
+  for (size_t h = 1; h < p.heads.size(); ++h) {
+    const HeadEntry& e0 = p.heads[0];
+    const HeadEntry& e = p.heads[h];
+    st->uniform = st->uniform && e.bits == e0.bits && e.gamma == e0.gamma && e.scales == e0.scales &&
+                  e.bypass_u == e0.bypass_u && e.bypass_w == e0.bypass_w && e.ref == e0.ref &&
+                  e.head_offset == (uint64_t)h * p.heads[1].head_offset;
+  }
   st->all32 = p.all32;
   st->hash = p.hash;
   st->geo = p.geo;

@@ -44,7 +44,22 @@ struct StepArgs {
   float* dg_acc;
   float* dg_ratio;
   uint32_t* dg_counts;
+  // every head alike (same width; RetNet: same gamma): the head table entry
+  // is `uni` with head_offset = h * uni_stride, so the kernels skip its load
+  int32_t uniform;
+  uint64_t uni_stride;
+  HeadEntry uni;
 };
+
+// Head table entry of head h.
+__device__ __forceinline__ HeadEntry head_entry(const StepArgs& a, int h) {
+  if (a.uniform) {
+    HeadEntry e = a.uni;
+    e.head_offset = (uint64_t)h * a.uni_stride;
+    return e;
+  }
+  return a.heads[h];
+}
 
 typedef void (*DecodeFn)(StepArgs);
 DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
