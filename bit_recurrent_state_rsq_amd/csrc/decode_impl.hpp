@@ -417,10 +417,24 @@ struct Decode {
   // w_j = beta (v_j - alpha u_j), broadcast to every lane of the column block.
   // xs: the lane's 8x8 values with S_ij = xs_ij * mul_i (mul = s/F, or 1 for an
   // fp32 tile); kap: k_i s_i / F when `fast` (exact products), unused otherwise.
+  // The gates and the lane's v values after the tree (`pre`, from dw_prefetch)
+  // are loaded at the start of the step with the state, not here.
+  struct DwPre {
+    float al, be, v[NSLOT];
+  };
+  static __device__ __forceinline__ DwPre dw_prefetch(const StepArgs& a, int tile, int j0, int lane) {
+    DwPre p;
+    p.al = a.alpha[tile];
+    p.be = a.beta[tile];
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) p.v[s] = kPW ? 0.f : load_in1(a, tile, j0 + xtree_col<NB>(s, lane));
+    return p;
+  }
+
   template <int BITS>
   static __device__ __forceinline__ void delta_w(const StepArgs& a, int tile, const float xs[8][8],
                                                  const float kf[8], const float mul[8], const float kap[8],
-                                                 bool fast, float wv[8], float* wl,
+                                                 bool fast, const DwPre& pre, float wv[8], float* wl,
                                                  float* up, int wrw, int wr, int j0, int lane, int wave) {
     float v8[8];
     if (fast) {
@@ -449,15 +463,14 @@ struct Decode {
     }
     xtree<NB>(v8, lane);
     across_waves(v8, up, wrw, wr, j0, lane, a.dv);
-    const float al = a.alpha[tile], be = a.beta[tile];
+    const float al = pre.al, be = pre.be;
     // lanes holding column sums compute w and publish it
     float* wrow = wl + wave * WC;
     const int lc = lane % CL;
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int c = xtree_col<NB>(s, lane);
-      const float vj = kPW ? 0.f : load_in1(a, tile, j0 + c);
-      const float w = __fmul_rn(be, __fsub_rn(vj, __fmul_rn(al, v8[s])));
+      const float w = __fmul_rn(be, __fsub_rn(pre.v[s], __fmul_rn(al, v8[s])));
       if (NB < 4 || ((lane >> 2) & 1) == 0) wrow[8 * lc + c] = w;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -580,6 +593,13 @@ struct Decode {
     load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
     load8(bf16, a.k, (size_t)tile * a.dk + i0, kf);
     decays(a, he, tile, i0, dec);
+    DwPre dwp{};
+    float wv[8];
+    if constexpr (MODEL == kGDN) dwp = dw_prefetch(a, tile, j0, lane);
+    else load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
+    // keep every load of the step above this point: issued together at the
+    // start, their latency overlaps instead of stalling the step midway
+    __builtin_amdgcn_sched_barrier(0);
 
     // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
     // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
@@ -616,13 +636,10 @@ struct Decode {
       }
     }
 
-    // update B_t: w = v, or the delta rule
-    float wv[8];
+    // update B_t: w = v (loaded at the start), or the delta rule
     if constexpr (MODEL == kGDN) {
-      delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kDense, wv, L.w, L.up, wrw, wr, j0,
+      delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kDense, dwp, wv, L.w, L.up, wrw, wr, j0,
                                      lane, wave);
-    } else {
-      load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
     }
 
     // decay and update; r = fl(c fl(a s)) kept for BDR
@@ -684,7 +701,7 @@ struct Decode {
           float ones[8], dummy[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) ones[i] = 1.f, dummy[i] = 0.f;
-          delta_w<8>(a, tile, xr, kf, ones, dummy, false, wr_, L.w, L.up + wrw * a.dv, wrw, wr, j0, lane, wave);
+          delta_w<8>(a, tile, xr, kf, ones, dummy, false, dwp, wr_, L.w, L.up + wrw * a.dv, wrw, wr, j0, lane, wave);
         } else {
           load8(bf16, a.v, (size_t)tile * a.dv + j0, wr_);
         }
