@@ -598,8 +598,10 @@ struct Decode {
     if constexpr (MODEL == kGDN) dwp = dw_prefetch(a, tile, j0, lane);
     else load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
     // keep every load of the step above this point: issued together at the
-    // start, their latency overlaps instead of stalling the step midway
-    __builtin_amdgcn_sched_barrier(0);
+    // start, their latency overlaps instead of stalling the step midway (not
+    // in the BDR, yoked and accounting variants, which already run at the
+    // register limit)
+    if constexpr (!(FEAT == kFeatBdr || kYoked || kDiag)) __builtin_amdgcn_sched_barrier(0);
 
     // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
     // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
@@ -1226,7 +1228,7 @@ DecodeFn decode_pick_feat(int feat) {
     case kFeatYoked: return decode_kernel<MODEL, CL, kFeatYoked, kSpecGeneric>;
     case kFeatDiag: return decode_kernel<MODEL, CL, kFeatDiag, kSpecGeneric>;
     case kFeatHad:
-      if constexpr (SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatHad, SPEC>;
+      if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatHad, SPEC>;
       else return decode_kernel<MODEL, CL, kFeatHad, SPEC>;
     case kFeatPW:
       if constexpr (MODEL == kGDN && SPEC == kSpecPersF16Bf16G32) return decode_kernel_occ<MODEL, CL, kFeatPW, SPEC>;
