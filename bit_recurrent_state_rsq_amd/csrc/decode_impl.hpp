@@ -1126,7 +1126,15 @@ struct Decode {
     L.z = L.op + wrw * a.dv;                  // [kMaxCap] + [nw][kMaxCap]
     uint32_t flags = 0;
 
-    if constexpr (kBypass) bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
+    // bypass: its loads join the state's (values held in registers) when
+    // they fit, else the column loop runs first
+    BypassRegs br;
+    bool byp_regs = false;
+    if constexpr (kBypass) {
+      byp_regs = bypass_regs_fit(a);
+      if (byp_regs) bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br);
+      else bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
+    }
     if constexpr (kPW) pw_phase(a, he, tb, tile, L.z);
 
     if constexpr (kF32) {
@@ -1138,6 +1146,9 @@ struct Decode {
         default: body<8>(a, he, tb, tile, L, flags); break;
       }
     }
+    if constexpr (kBypass) {
+      if (byp_regs) bypass_store(a, he, tb, tile, SP::bf16(a), br, L.z);
+    }
     if constexpr (kPW) {
       // every wavefront has read the leaving pair: the new one takes its slot
       __syncthreads();
@@ -1146,18 +1157,20 @@ struct Decode {
     if (wrw > 1 || kBypass || kPW) {
       __syncthreads();
       // combine readout partials over row-wavefronts, add the bypass term, store o
-      combine_o(a, he, tb, tile, L, wrw, flags);
+      combine_o(a, he, tb, tile, L, wrw, flags, byp_regs, br);
     }
     finish(a, tile, flags);
   }
 
   static __device__ __forceinline__ void combine_o(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
-                                                   int tile, const Lds& L, int wrw, uint32_t& flags) {
+                                                   int tile, const Lds& L, int wrw, uint32_t& flags,
+                                                   bool byp_regs, BypassRegs& br) {
     // bypass columns (fp16) / window pairs (E4M3): cnt columns of W, each
     // weighted by its z. The sum W z is spread over every thread of the
     // block: thread (p, j) takes columns p, p + P, ... of row j of W (its
     // loads in flight together), the P partials meet in LDS (L.up, free here:
-    // P d_v <= 2 wrw d_v floats).
+    // P d_v <= 2 wrw d_v floats). The bypass's register path holds its W
+    // entries in registers already.
     constexpr bool kWz = kBypass || kPW;
     const int cnt = kBypass ? a.n + 1 : kPW ? (a.n < a.pw ? a.n + 1 : a.pw) : 0;
     const int P = kWz ? (int)(blockDim.x / a.dv) : 0;
@@ -1169,7 +1182,9 @@ struct Decode {
       const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
       if (pp < P) {
         float part = 0.f;
-        for (int c = pp; c < cnt; c += P) part = __builtin_fmaf(wval(c, j), L.z[c], part);
+        if (kBypass && byp_regs) part = bypass_wz_part(a, SP::bf16(a), br, L.z);
+        else
+          for (int c = pp; c < cnt; c += P) part = __builtin_fmaf(wval(c, j), L.z[c], part);
         L.up[pp * a.dv + j] = part;
       }
       __syncthreads();

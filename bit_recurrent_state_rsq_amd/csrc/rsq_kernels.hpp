@@ -145,4 +145,150 @@ __device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const Hea
   __syncthreads();
 }
 
+// The same bypass step with every load issued at kernel start, next to the
+// state's own, and held in registers until the state's step is done. The
+// loop above waits on a round trip per column, and on gfx9 a wait for a
+// load also waits for every store issued before it, so there each column
+// costs a load and a store round trip. Here the decay, the stores and the
+// sums run after the state's step, with nothing left to wait for.
+// Holds for d_k <= 256 (four rows per lane), at most kBypCols columns per
+// wavefront and, for the readout term, at most kBypWCols columns per
+// partial-sum thread group (P = blockDim / d_v groups).
+constexpr int kBypCols = 4, kBypWCols = 8;
+struct BypassRegs {
+  // raw loaded bits: nothing is converted until bypass_store, after the
+  // state's own loads have been issued. Lane l holds rows 4l .. 4l + 3.
+  uint32_t qb[4];              // q_i (bf16 pairs in qb[0..1], or 4 fp32)
+  float av[4];                 // a_i
+  uint32_t kb[4];              // k_i (used by the wavefront that writes column n)
+  uint32_t uv[kBypCols][2];    // U_ic of the wavefront's columns (binary16 pairs)
+  uint32_t wv[kBypWCols];      // W_jc of this thread's readout columns (binary16 bits)
+  uint32_t vb;                 // v_j (column n of W is fp16(v_j))
+};
+
+__device__ __forceinline__ bool bypass_regs_fit(const StepArgs& a) {
+  const int nw = blockDim.x >> 6, P = (int)(blockDim.x / a.dv);
+  return a.dk <= 256 && a.n + 1 <= kBypCols * nw && P >= 1 && a.n + 1 <= kBypWCols * P;
+}
+
+__device__ __forceinline__ uint32_t in_bits(bool bf16, const void* p, size_t idx) {
+  if (bf16) return reinterpret_cast<const uint16_t*>(p)[idx];
+  return reinterpret_cast<const uint32_t*>(p)[idx];
+}
+__device__ __forceinline__ float bits_in(bool bf16, uint32_t b) { return __uint_as_float(bf16 ? b << 16 : b); }
+// four consecutive inputs from element idx (a multiple of 4): bf16 as two
+// words in w[0..1], fp32 as four
+__device__ __forceinline__ void in4_bits(bool bf16, const void* p, size_t idx, uint32_t w[4]) {
+  if (bf16) {
+    const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(p) + idx);
+    w[0] = t.x, w[1] = t.y, w[2] = 0u, w[3] = 0u;
+  } else {
+    const uint4 t = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint32_t*>(p) + idx);
+    w[0] = t.x, w[1] = t.y, w[2] = t.z, w[3] = t.w;
+  }
+}
+__device__ __forceinline__ float in4_at(bool bf16, const uint32_t w[4], int r) {
+  if (bf16) return __uint_as_float((r & 1) ? (w[r >> 1] & 0xFFFF0000u) : (w[r >> 1] << 16));
+  return __uint_as_float(w[r]);
+}
+// pins a loaded value to this point of the program: the conversions that
+// follow stay here instead of being hoisted next to the load (which would
+// make the load's wait come early)
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+// Every load is unconditional, at an index clamped into the tile's sections
+// (values past n or d_k are loaded and dropped): no branch separates the
+// loads, so they all leave before the first wait. Four consecutive rows per
+// lane make each column one 8-byte load.
+__device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& he, const uint8_t* tb, int tile,
+                                            int model, bool bf16, BypassRegs& br) {
+  const uint16_t* U = reinterpret_cast<const uint16_t*>(tb + he.bypass_u);
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(tb + he.bypass_w);
+  const int last = a.cap - 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int i4 = min(4 * lane, a.dk - 4);
+  in4_bits(bf16, a.q, (size_t)tile * a.dk + i4, br.qb);
+  in4_bits(bf16, a.k, (size_t)tile * a.dk + i4, br.kb);
+  if (model == kGLA) {
+    const float4 t = *reinterpret_cast<const float4*>(a.alpha + (size_t)tile * a.dk + i4);
+    br.av[0] = t.x, br.av[1] = t.y, br.av[2] = t.z, br.av[3] = t.w;
+  } else {
+    const float d = row_decay(a, he, model, tile, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) br.av[r] = d;
+  }
+#pragma unroll
+  for (int m = 0; m < kBypCols; ++m) {
+    const int c = min(wave + nw * m, last);
+    const uint2 t = *reinterpret_cast<const uint2*>(U + (size_t)c * a.dk + i4);
+    br.uv[m][0] = t.x, br.uv[m][1] = t.y;
+  }
+  // readout term: thread (pp, j) takes columns pp, pp + P, ... (column n is
+  // fp16(v_j), written this step: taken from v, not read back)
+  const int P = (int)(blockDim.x / a.dv);
+  const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
+#pragma unroll
+  for (int m = 0; m < kBypWCols; ++m) br.wv[m] = W[(size_t)min(pp + P * m, last) * a.dv + j];
+  br.vb = in_bits(bf16, a.v, (size_t)tile * a.dv + j);
+}
+
+// Decay and store of U, the new columns of U and W, and z_c = sum_i U_ic q_i
+// in lds_z (the lane's four rows in order, then a wave reduction).
+__device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
+                                             bool bf16, BypassRegs& br, float* lds_z) {
+  uint16_t* U = reinterpret_cast<uint16_t*>(tb + he.bypass_u);
+  __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
+  const int n = a.n;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const bool rows_ok = 4 * lane < a.dk;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    pin(br.qb[r]);
+    pin(br.av[r]);
+    pin(br.kb[r]);
+  }
+#pragma unroll
+  for (int m = 0; m < kBypCols; ++m) {
+    const int c = wave + nw * m;
+    if (c > n) break;
+    pin(br.uv[m][0]);
+    pin(br.uv[m][1]);
+    float acc = 0.f;
+    uint16_t un[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __half u = __ushort_as_half((uint16_t)(br.uv[m][r >> 1] >> (16 * (r & 1))));
+      const __half h = c < n ? mul_rn_half(br.av[r], u) : __float2half_rn(in4_at(bf16, br.kb, r));
+      un[r] = __half_as_ushort(h);
+      acc = __builtin_fmaf(__half2float(h), in4_at(bf16, br.qb, r), acc);
+    }
+    if (rows_ok)
+      *reinterpret_cast<uint2*>(U + (size_t)c * a.dk + 4 * lane) =
+          make_uint2((uint32_t)un[0] | ((uint32_t)un[1] << 16), (uint32_t)un[2] | ((uint32_t)un[3] << 16));
+    acc = wave_sum64(rows_ok ? acc : 0.f);
+    if (lane == 0) lds_z[c] = acc;
+  }
+  const int P = (int)(blockDim.x / a.dv);
+  const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
+  pin(br.vb);
+  if (pp == n % P) W[(size_t)n * a.dv + j] = __float2half_rn(bits_in(bf16, br.vb));   // column n of row j
+}
+
+// Readout term of the register path: this thread's share of (W z)_j.
+__device__ __forceinline__ float bypass_wz_part(const StepArgs& a, bool bf16, BypassRegs& br, const float* lds_z) {
+  const int P = (int)(blockDim.x / a.dv);
+  const int pp = threadIdx.x / a.dv;
+  const int cnt = a.n + 1;
+  float part = 0.f;
+#pragma unroll
+  for (int m = 0; m < kBypWCols; ++m) {
+    const int c = pp + P * m;
+    pin(br.wv[m]);
+    const __half wh = c == a.n ? __float2half_rn(bits_in(bf16, br.vb)) : __ushort_as_half((uint16_t)br.wv[m]);
+    if (c < cnt) part = __builtin_fmaf(__half2float(wh), lds_z[c], part);
+  }
+  return part;
+}
+
 }  // namespace rsq
