@@ -759,13 +759,13 @@ struct Decode {
           for (int k = 0; k < 4; ++k) {
             const uint32_t mine = __float_as_uint(h2 ? lm[4 + k] : lm[k]);
             const uint32_t other = __float_as_uint(h2 ? lm[k] : lm[4 + k]);
-            kp[k] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x4E, 0xF, 0xF, false));
+            kp[k] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x4E, 0xF, 0xF, false));
           }
           float m2[2], so[2], ratio[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const uint32_t mine = h1 ? kp[2 + k] : kp[k], other = h1 ? kp[k] : kp[2 + k];
-            m2[k] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0xB1, 0xF, 0xF, false)));
+            m2[k] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0xB1, 0xF, 0xF, false)));
             so[k] = h2 ? (h1 ? s_old[6 + k] : s_old[4 + k]) : (h1 ? s_old[2 + k] : s_old[k]);
           }
           if (smode == kScalePersistent) {
@@ -802,17 +802,15 @@ struct Decode {
             if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
             tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
           }
-          // all-gather of the reciprocals: quad lane q^1, then q^2
-          float g4[4], p2[4];
-          const float p1a = dpp_xor1(iv[0]), p1b = dpp_xor1(iv[1]);
-          g4[0] = h1 ? p1a : iv[0];
-          g4[1] = h1 ? p1b : iv[1];
-          g4[2] = h1 ? iv[0] : p1a;
-          g4[3] = h1 ? iv[1] : p1b;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p2[j] = dpp_xor2(g4[j]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) inv[i] = ((i >> 2) != 0) == h2 ? g4[i & 3] : p2[i & 3];
+          // all-gather of the reciprocals: row 2q + b comes from quad lane q
+          inv[0] = dpp_quad_bcast<0>(iv[0]);
+          inv[1] = dpp_quad_bcast<0>(iv[1]);
+          inv[2] = dpp_quad_bcast<1>(iv[0]);
+          inv[3] = dpp_quad_bcast<1>(iv[1]);
+          inv[4] = dpp_quad_bcast<2>(iv[0]);
+          inv[5] = dpp_quad_bcast<2>(iv[1]);
+          inv[6] = dpp_quad_bcast<3>(iv[0]);
+          inv[7] = dpp_quad_bcast<3>(iv[1]);
         }
       } else if constexpr (kSplit8) {
         const int q = lane & 7;
@@ -828,17 +826,17 @@ struct Decode {
         for (int r = 0; r < 4; ++r) {
           const uint32_t mine = __float_as_uint(h4 ? lm[4 + r] : lm[r]);
           const uint32_t other = __float_as_uint(h4 ? lm[r] : lm[4 + r]);
-          k4[r] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x141, 0xF, 0xF, false));
+          k4[r] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x141, 0xF, 0xF, false));
         }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const uint32_t mine = h2 ? k4[2 + r] : k4[r], other = h2 ? k4[r] : k4[2 + r];
-          k2[r] = max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0x4E, 0xF, 0xF, false));
+          k2[r] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x4E, 0xF, 0xF, false));
         }
         float m1[2], so1, ratio[2];
         {
           const uint32_t mine = h1 ? k2[1] : k2[0], other = h1 ? k2[0] : k2[1];
-          m1[0] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_mov_dpp((int)other, 0xB1, 0xF, 0xF, false)));
+          m1[0] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0xB1, 0xF, 0xF, false)));
           m1[1] = m1[0];
           const float a4 = h4 ? s_old[4] : s_old[0], b4 = h4 ? s_old[5] : s_old[1];
           const float c4 = h4 ? s_old[6] : s_old[2], d4 = h4 ? s_old[7] : s_old[3];
