@@ -9,7 +9,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <map>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "rsq.h"
@@ -281,9 +284,21 @@ rsq_status launch(rsq::DecodeFn fn, const rsq_state* st, const StepArgs& a, void
   const dim3 grid(st->cfg.batch * st->cfg.heads), block(st->geo.threads);
   if (lds == 0) lds = st->geo.lds;
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return hip_fail(e, "raising the kernel's LDS limit");
+    // raised once per kernel and device, to the largest size a launch has
+    // asked for (the attribute call is host work that need not repeat every step)
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> raised;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "current device");
+    const auto key = std::make_pair(dev, reinterpret_cast<const void*>(fn));
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = raised.find(key);
+    if (it == raised.end() || it->second < lds) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return hip_fail(e, "raising the kernel's LDS limit");
+      raised[key] = lds;
+    }
   }
   if (ev_start || ev_stop) {
     // the events ride on the dispatch packet itself: no marker enters the stream
