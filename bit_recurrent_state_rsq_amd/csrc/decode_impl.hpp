@@ -248,8 +248,97 @@ struct Spec {
 // l R .. l R + R - 1 (R = d_k / 64, or one row for d_k < 64, lanes past d_k
 // adding zeros), so the in-lane tree and then the butterfly over lanes 1, 2,
 // ..., 32 apart give the cascade order. The new pair's z_s = sum_i e4m3(k_i) q_i.
-static __device__ __noinline__ void pw_pairs(uint8_t* U, const void* kp, const void* qp, bool bf16, int tile, int dk, int W,
+// The same for d_k <= 256 (R <= 4 rows per lane) and at most 4 pairs per
+// wavefront: the lane's key bytes of a pair are one dword, loaded for every
+// pair before the first wait, and written back with one store. Same sums in
+// the same order as pw_pairs.
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) uint8_t g_u8;
+template <bool BF16>
+static __device__ __noinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, const void* qp, int tile, int dk, int W,
+                                              int n, int slot, float al, float be, float* z) {
+  const bool leaving = n == W;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int R = dk >= 64 ? dk >> 6 : 1;   // 1, 2 or 4
+  const int i0 = lane * R;                 // the lane's first row
+  const bool rows_ok = i0 < dk;
+  g_u32* U = (g_u32*)reinterpret_cast<uint32_t*>(U8);
+  const g_u16* K16 = (const g_u16*)reinterpret_cast<const uint16_t*>(kp);
+  const g_u16* Q16 = (const g_u16*)reinterpret_cast<const uint16_t*>(qp);
+  const g_u32* K32 = (const g_u32*)reinterpret_cast<const uint32_t*>(kp);
+  const g_u32* Q32 = (const g_u32*)reinterpret_cast<const uint32_t*>(qp);
+  uint32_t pre[4], kb[4], qb[4];
+  const int wi = min(i0, dk - 1) >> 2, sh = 8 * (i0 & 3);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) pre[m] = U[(size_t)min(wave + nw * m, W - 1) * (dk >> 2) + wi];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const size_t idx = (size_t)tile * dk + min(i0 + e, dk - 1);
+    kb[e] = BF16 ? (uint32_t)K16[idx] << 16 : K32[idx];
+    qb[e] = BF16 ? (uint32_t)Q16[idx] << 16 : Q32[idx];
+  }
+  float k4[4], q4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bool ok = e < R && rows_ok;
+    k4[e] = ok ? __uint_as_float(kb[e]) : 0.f;
+    q4[e] = ok ? __uint_as_float(qb[e]) : 0.f;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int c = wave + nw * m;
+    if (c >= W) break;
+    const bool is_new = c == slot;
+    const bool stays = c < n && !(leaving && c == slot);
+    if (!is_new && !stays) continue;
+    float zacc = 0.f;
+    if (is_new) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(k4[e])), q4[e], zacc);
+    } else {
+      const uint32_t ub = pre[m] >> sh;
+      float ue[4], pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ue[e] = (e < R && rows_ok) ? e4m3_to_f32((ub >> (8 * e)) & 0xFFu) : 0.f;
+        pe[e] = __fmul_rn(k4[e], ue[e]);
+      }
+      if (1 < R) { pe[0] = __fadd_rn(pe[0], pe[1]); pe[2] = __fadd_rn(pe[2], pe[3]); }
+      if (2 < R) pe[0] = __fadd_rn(pe[0], pe[2]);
+      float d = pe[0];
+      d = __fadd_rn(d, dpp_xor1(d));
+      d = __fadd_rn(d, dpp_xor2(d));
+      d = __fadd_rn(d, swz_xor(d, 4));
+      d = __fadd_rn(d, dpp_ror8(d));
+      d = __fadd_rn(d, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(d), 0x401F)));
+      d = __fadd_rn(d, __shfl_xor(d, 32, 64));
+      const float b = __fmul_rn(be, d);
+      uint32_t codes = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t code = f32_to_e4m3(__fmul_rn(al, __fsub_rn(ue[e], __fmul_rn(b, k4[e]))));
+        if (e < R) {
+          codes |= code << (8 * e);
+          zacc = __builtin_fmaf(e4m3_to_f32(code), q4[e], zacc);
+        }
+      }
+      if (rows_ok) {
+        g_u8* dst = (g_u8*)(U8 + (size_t)c * dk + i0);
+        if (R == 4) *(g_u32*)dst = codes;
+        else if (R == 2) *(g_u16*)dst = (uint16_t)codes;
+        else *dst = (uint8_t)codes;
+      }
+    }
+    zacc = wave_sum64(zacc);
+    if (lane == 0) z[c] = zacc;
+  }
+}
+
+template <bool BF16>
+static __device__ __noinline__ void pw_pairs(uint8_t* U, const void* kp, const void* qp, int tile, int dk, int W,
                                            int n, int slot, float al, float be, float* z) {
+  constexpr bool bf16 = BF16;
   const bool leaving = n == W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int R = dk >= 64 ? dk >> 6 : 1;   // rows per lane: 1 .. 16, a power of two
@@ -257,17 +346,33 @@ static __device__ __noinline__ void pw_pairs(uint8_t* U, const void* kp, const v
   float k4[4], q4[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    // unconditional loads at a clamped index (no branch between the loads)
     const int i = lane * R + e;
     const bool ok = e < R && i < dk;
-    k4[e] = ok ? in_elem(bf16, kp, (size_t)tile * dk + i) : 0.f;
-    q4[e] = ok ? in_elem(bf16, qp, (size_t)tile * dk + i) : 0.f;
+    const float kv = in_elem(bf16, kp, (size_t)tile * dk + min(i, dk - 1));
+    const float qv = in_elem(bf16, qp, (size_t)tile * dk + min(i, dk - 1));
+    k4[e] = ok ? kv : 0.f;
+    q4[e] = ok ? qv : 0.f;
   }
   auto kq = [&](int e, float& ke, float& qe) {
     const int i = lane * R + e;
     ke = in_elem(bf16, kp, (size_t)tile * dk + i);
     qe = in_elem(bf16, qp, (size_t)tile * dk + i);
   };
-  for (int c = wave; c < W; c += nw) {
+  // the lane's R <= 4 key bytes of the wavefront's first four pairs, one
+  // load each and all issued before the first wait (a later load would
+  // otherwise also wait for the stores of the pair before it)
+  constexpr int kPre = 4;
+  uint32_t pre[kPre];
+  const bool preload = R <= 4;
+  if (preload) {
+    const uint32_t* U32 = reinterpret_cast<const uint32_t*>(U);
+    const int wi = min(lane * R, dk - 1) >> 2;
+#pragma unroll
+    for (int m = 0; m < kPre; ++m) pre[m] = U32[(size_t)min(wave + nw * m, W - 1) * (dk >> 2) + wi];
+  }
+  int m = 0;
+  for (int c = wave; c < W; c += nw, ++m) {
     const bool is_new = c == slot;
     const bool stays = c < n && !(leaving && c == slot);
     if (!is_new && !stays) continue;
@@ -299,7 +404,15 @@ static __device__ __noinline__ void pw_pairs(uint8_t* U, const void* kp, const v
           const int r = blk * 4 + e, i = lane * R + r;
           float ue = 0.f, ke = 0.f, qe = 0.f;
           if (r < R && i < dk) {
-            ue = e4m3_to_f32(uc[i]);
+            uint32_t byte = 0;
+            if (blk == 0 && preload && m < kPre) {
+#pragma unroll
+              for (int mm = 0; mm < kPre; ++mm)
+                if (mm == m) byte = (pre[mm] >> (8 * ((i & 3)))) & 0xFFu;
+            } else {
+              byte = uc[i];
+            }
+            ue = e4m3_to_f32(byte);
             if (blk == 0) ke = k4[e];
             else kq(r, ke, qe);
           }
@@ -1091,8 +1204,14 @@ struct Decode {
   // the body's.
   static __device__ __forceinline__ void pw_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                                   float* z) {
-    pw_pairs(tb + he.bypass_u, a.k, a.q, SP::bf16(a), tile, a.dk, a.pw, a.n, (int)((a.t_next - 1) % a.pw),
-             a.alpha[tile], a.beta[tile], z);
+    const int slot = (int)((a.t_next - 1) % a.pw);
+    if (a.dk <= 256 && a.pw <= 4 * (int)(blockDim.x >> 6)) {
+      if (SP::bf16(a)) pw_pairs_r4<true>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
+      else pw_pairs_r4<false>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
+      return;
+    }
+    if (SP::bf16(a)) pw_pairs<true>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
+    else pw_pairs<false>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
   }
 
   // The new pure write (e4m3(k_t), e4m3(fl(beta_t v_t))) into slot (t - 1) mod W.
@@ -1133,7 +1252,6 @@ struct Decode {
       if (byp_regs) bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br);
       else bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
     }
-    if constexpr (kPW) pw_phase(a, he, tb, tile, L.z);
 
     if constexpr (kF32) {
       body<32>(a, he, tb, tile, L, flags);
@@ -1147,6 +1265,10 @@ struct Decode {
     if constexpr (kBypass) {
       if (byp_regs) bypass_store(a, he, tb, tile, SP::bf16(a), br, L.z);
     }
+    // the staying window pairs: after the state's step, whose loads then go
+    // out first (the pairs never touch the leaving pair's slot, which the
+    // state's step reads)
+    if constexpr (kPW) pw_phase(a, he, tb, tile, L.z);
     if constexpr (kPW) {
       // every wavefront has read the leaving pair: the new one takes its slot
       __syncthreads();

@@ -35,22 +35,27 @@ constexpr int kMaxCap = 32;   // bypass columns a kernel can hold
 // infinities): round to nearest-even, saturate to +-448, NaN -> 0x7F with the
 // sign kept. Below 2^-6 the grid is the multiples of 2^-9 (a * 512 is exact).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  // branch-free: the subnormal and normal encodings are both formed and one
+  // is selected (below 2^-6 the code is RNE(|x| 512), codes 0 .. 8)
   const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
   const float a = fabsf(x);
-  if (!(a == a)) return sign | 0x7Fu;
-  if (a < 0x1p-6f) return sign | (uint32_t)__builtin_rintf(a * 512.f);   // 8 is 2^-6, code 0x08
+  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(a, 1.f) * 512.f);
   uint32_t r = __float_as_uint(a);
   r = (r + 0x7FFFFu + ((r >> 20) & 1u)) & 0xFFF00000u;                    // RNE to 3 mantissa bits
   const uint32_t e = (r >> 23) - 120u, m = (r >> 20) & 7u;                 // exponent field, bias 7
-  if (e > 15u || (e == 15u && m == 7u)) return sign | 0x7Eu;              // saturate to 448
-  return sign | (e << 3) | m;
+  const uint32_t nor = (e > 15u || (e == 15u && m == 7u)) ? 0x7Eu : ((e << 3) | m);   // saturate to 448
+  uint32_t c = a < 0x1p-6f ? sub : nor;
+  c = (a == a) ? c : 0x7Fu;
+  return sign | c;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if (e == 15u && m == 7u) v = __builtin_nanf("");
-  return (c & 0x80u) ? -v : v;
+  const float sub = (float)m * 0x1p-9f;
+  const float nor = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  float v = e == 0 ? sub : nor;
+  v = (c & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : v;
+  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
 }
 
 // Round-to-nearest-even of an exact product through the float32 adder:
