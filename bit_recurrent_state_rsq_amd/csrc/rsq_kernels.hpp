@@ -205,7 +205,9 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
                                             int model, bool bf16, BypassRegs& br) {
   const uint16_t* U = reinterpret_cast<const uint16_t*>(tb + he.bypass_u);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(tb + he.bypass_w);
-  const int last = a.cap - 1;
+  // column indices clamp to the last column the step uses (U: n - 1, W: n),
+  // so the loads past it hit lines already fetched instead of new ones
+  const int ulast = max(a.n - 1, 0), wlast = a.n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int i4 = min(4 * lane, a.dk - 4);
   in4_bits(bf16, a.q, (size_t)tile * a.dk + i4, br.qb);
@@ -220,7 +222,7 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
   }
 #pragma unroll
   for (int m = 0; m < kBypCols; ++m) {
-    const int c = min(wave + nw * m, last);
+    const int c = min(wave + nw * m, ulast);
     const uint2 t = *reinterpret_cast<const uint2*>(U + (size_t)c * a.dk + i4);
     br.uv[m][0] = t.x, br.uv[m][1] = t.y;
   }
@@ -229,7 +231,7 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
   const int P = (int)(blockDim.x / a.dv);
   const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
 #pragma unroll
-  for (int m = 0; m < kBypWCols; ++m) br.wv[m] = W[(size_t)min(pp + P * m, last) * a.dv + j];
+  for (int m = 0; m < kBypWCols; ++m) br.wv[m] = W[(size_t)min(pp + P * m, wlast) * a.dv + j];
   br.vb = in_bits(bf16, a.v, (size_t)tile * a.dv + j);
 }
 
