@@ -113,6 +113,7 @@ class Tally:
         self.forgiven = 0
         self.mismatch = 0
         self.steps = 0
+        self.oracle_flags = 0   # status bits the oracle raised on the checked steps
 
     def check(self):
         assert self.mismatch == 0, "%d code/scale mismatches outside the decision windows" % self.mismatch
@@ -122,6 +123,7 @@ class Tally:
 
 def compare(post, new, diag, o_gpu, o_ref, w, tally, what=""):
     """Compare one checked step. `post` GPU arrays, `new` oracle OState."""
+    tally.oracle_flags |= int(getattr(new, "flags", 0))
     if "S32" in post:
         assert np.array_equal(post["S32"], new.S32.astype(np.float32)), what + " fp32 state differs"
         assert rel_l2(o_gpu, o_ref) <= REL_STEP, what + " o rel-L2 %g" % rel_l2(o_gpu, o_ref)

@@ -323,6 +323,9 @@ def test_cfg3_gla_full_horizon_with_merges():
     ("gla", 6, 16, "persistent", "f16", 128, 64, 3, 4, True),
     ("gla", 4, 128, "dynamic", "f16", 64, 128, 1, 3, True),
     ("retnet", 8, 32, "dynamic", "f32", 256, 32, 0, 4, True),
+    # the bypass column loop: one wavefront with more than four columns, and d_k > 256
+    ("gla", 4, 64, "dynamic", "f16", 64, 64, 2, 6, True),
+    ("retnet", 4, 32, "dynamic", "f16", 512, 32, 2, 3, False),
 ])
 def test_merge_variants(model, bits, g, mode, sdt, dk, dv, k, m, bdr):
     base = {"retnet": CONFIGS[0], "mamba2": CONFIGS[2], "gla": CONFIGS[3]}[model]

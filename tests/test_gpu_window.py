@@ -31,6 +31,10 @@ def _w(**kw):
     dict(bits=6, group=16, d_v=32, pw_window=2, in_dtype="f32"),
     dict(d_k=64, group=64, d_v=64, pw_window=6),
     dict(d_k=32, group=128, d_v=128, pw_window=7, scale_dtype="f32"),
+    # the general pair transition: eight rows per lane (d_k = 512), and more
+    # pairs than four per wavefront (one wavefront, W = 6)
+    dict(d_k=512, d_v=32, pw_window=4),
+    dict(d_v=32, pw_window=6),
 ])
 def test_window_step_matches_oracle(kw):
     w = _w(**kw)
@@ -40,7 +44,9 @@ def test_window_step_matches_oracle(kw):
     tally, st = run_parity(w, steps, check_steps=range(1, steps + 1))
     tally.check()
     assert st.counters() == (steps, W)
-    assert st.get_status() == 0
+    # every step is checked, so the sticky status word holds exactly the bits
+    # the oracle raised (a decayed history with tiny binary16 steps can clip)
+    assert st.get_status() == tally.oracle_flags
 
 
 def test_window_cfg1_shape_sampled():
