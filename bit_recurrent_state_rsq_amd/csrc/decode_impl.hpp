@@ -469,7 +469,7 @@ struct Decode {
   static constexpr bool kHad = FEAT == kFeatHad;
   // pure-write window (Gated DeltaNet): the history takes the transition with v = 0
   static constexpr bool kPW = FEAT == kFeatPW;
-  static constexpr bool kDense = kF32 || kHad || kPW;
+  static constexpr bool kDense = kF32 || kPW;
   // BDR needs the pre-rounding x next to the codes; so do the diagnostics
   static constexpr bool kKeepX = !kF32 && (FEAT == kFeatBdr || kYoked || kDiag);
 
@@ -533,14 +533,18 @@ struct Decode {
   // The gates and the lane's v values after the tree (`pre`, from dw_prefetch)
   // are loaded at the start of the step with the state, not here.
   struct DwPre {
-    float al, be, v[NSLOT];
+    float al, be, v[kHad ? 8 : NSLOT];   // the rotation needs v of the lane's own 8 columns
   };
   static __device__ __forceinline__ DwPre dw_prefetch(const StepArgs& a, int tile, int j0, int lane) {
     DwPre p;
     p.al = a.alpha[tile];
     p.be = a.beta[tile];
+    if constexpr (kHad) {
+      load8(SP::bf16(a), a.v, (size_t)tile * a.dv + j0, p.v);
+    } else {
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) p.v[s] = kPW ? 0.f : load_in1(a, tile, j0 + xtree_col<NB>(s, lane));
+      for (int s = 0; s < NSLOT; ++s) p.v[s] = kPW ? 0.f : load_in1(a, tile, j0 + xtree_col<NB>(s, lane));
+    }
     return p;
   }
 
@@ -577,53 +581,63 @@ struct Decode {
     xtree<NB>(v8, lane);
     across_waves(v8, up, wrw, wr, j0, lane, a.dv);
     const float al = pre.al, be = pre.be;
-    // lanes holding column sums compute w and publish it
+    // lanes holding column sums compute w and publish it (INT4+Had: they
+    // publish the rotated sums u~, and every lane forms w for its own
+    // columns from u = u~ H / g, then rotates it: w~ = H w)
     float* wrow = wl + wave * WC;
     const int lc = lane % CL;
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int c = xtree_col<NB>(s, lane);
-      const float w = __fmul_rn(be, __fsub_rn(pre.v[s], __fmul_rn(al, v8[s])));
+      const float w = kHad ? v8[s] : __fmul_rn(be, __fsub_rn(pre.v[s], __fmul_rn(al, v8[s])));
       if (NB < 4 || ((lane >> 2) & 1) == 0) wrow[8 * lc + c] = w;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     loadf8(wrow + 8 * lc, wv);
+    if constexpr (kHad) {
+      const int gl = SP::GL > 0 ? SP::GL : (a.group >> 3);
+      const float ig = 1.0f / (float)(8 * gl);   // 1/g, a power of two
+      fwht8(wv, gl, lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float u = __fmul_rn(wv[j], ig);
+        wv[j] = __fmul_rn(be, __fsub_rn(pre.v[j], __fmul_rn(al, u)));
+      }
+      fwht8(wv, gl, lane);
+    }
   }
 
-  // Unnormalised Walsh-Hadamard transform of each row's scale group
-  // (INT4+Had of "Preserving Updates ...", Table 2): butterflies at column
-  // distance 1, 2, 4 inside the lane's 8 columns, then 8, 16, ... across the
-  // group's gl lanes (lane bit m = column bit 8m), each pair (a, b) at
-  // (j, j + h) becoming (fl(a + b), fl(a - b)).
-  static __device__ __forceinline__ void fwht_rows(float x[8][8], int gl, int lane) {
+  // Unnormalised Walsh-Hadamard transform of the lane's share of a vector
+  // whose scale groups run along the columns (INT4+Had of "Preserving
+  // Updates ...", Table 2): butterflies at column distance 1, 2, 4 inside the
+  // lane's 8 columns, then 8, 16, ... across the group's gl lanes (lane bit m
+  // = column bit 8m), each pair (a, b) at (j, j + h) becoming
+  // (fl(a + b), fl(a - b)). Across lanes the partner's value p arrives by
+  // DPP / swizzle, and fma(sign, x, p) forms fl(x + p) on the lower lane,
+  // fl(p - x) on the upper.
+  static __device__ __forceinline__ void fwht8(float v[8], int gl, int lane) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if ((j & h) == 0) {
-            const float lo = x[i][j], hi = x[i][j + h];
-            x[i][j] = __fadd_rn(lo, hi);
-            x[i][j + h] = __fsub_rn(lo, hi);
-          }
-    // across lanes: the partner's value p arrives by DPP / swizzle, and
-    // fma(sign, x, p) forms fl(x + p) on the lower lane, fl(p - x) on the upper
+      for (int j = 0; j < 8; ++j)
+        if ((j & h) == 0) {
+          const float lo = v[j], hi = v[j + h];
+          v[j] = __fadd_rn(lo, hi);
+          v[j + h] = __fsub_rn(lo, hi);
+        }
 #pragma unroll
     for (int lvl = 0; lvl < 4; ++lvl) {
       const int m = 1 << lvl;
       if (m >= gl) break;
       const float sg = (lane & m) ? -1.f : 1.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = x[i][j];
-          const float p = lvl == 0 ? dpp_xor1(v) : lvl == 1 ? dpp_xor2(v) : lvl == 2 ? swz_xor(v, 4) : dpp_ror8(v);
-          x[i][j] = __builtin_fmaf(sg, v, p);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float x = v[j];
+        const float p = lvl == 0 ? dpp_xor1(x) : lvl == 1 ? dpp_xor2(x) : lvl == 2 ? swz_xor(x, 4) : dpp_ror8(x);
+        v[j] = __builtin_fmaf(sg, x, p);
+      }
     }
   }
 
@@ -661,19 +675,6 @@ struct Decode {
       load_chunk<BITS>(cp, ch);
       load_scales8(sf16, sp, s_old);
       unpack_scaled(ch, x);
-      if constexpr (kHad) {
-        // the stored group is y = x H: back to x = fl(fl(c s) H) / g
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(__fmul_rn(x[i][j], invF), s_old[i]);
-        fwht_rows(x, gl, lane);
-        const float ig = 1.0f / (float)(8 * gl);   // 1/g, a power of two
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(x[i][j], ig);
-      }
       if constexpr (kPW) {
         // dense history fl(c s); the pair written W steps ago leaves the
         // window and joins it before the transition: hd = fma(u_i, w_j, h)
@@ -751,7 +752,9 @@ struct Decode {
       }
     }
 
-    // update B_t: w = v (loaded at the start), or the delta rule
+    // update B_t: w = v (loaded at the start), or the delta rule; INT4+Had
+    // steps in the rotated basis, so its update vector is w~ = H w
+    if constexpr (kHad && MODEL != kGDN) fwht8(wv, gl, lane);
     if constexpr (MODEL == kGDN) {
       delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kDense, dwp, wv, L.w, L.up, wrw, wr, j0,
                                      lane, wave);
@@ -782,7 +785,7 @@ struct Decode {
       }
       xtree<NB>(o8, lane);
       const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
-      if (wrw == 1 && !kBypass && !kPW) {
+      if (wrw == 1 && !kBypass && !kPW && !kHad) {
         // one wavefront covers every row: its sums are the readout
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
@@ -804,8 +807,6 @@ struct Decode {
       constexpr int qmax = Fmt<BITS>::qmax;
       constexpr float qmaxf = (float)qmax;
       constexpr float magic = Fmt<BITS>::magic;
-      // INT4+Had quantizes the rotated group y = x H
-      if constexpr (kHad) fwht_rows(x, gl, lane);
       // yoked reference: the same recurrence on an fp32 tile; absmax comes from it
       float xr[kYoked ? 8 : 1][8];
       if constexpr (kYoked) {
@@ -1274,7 +1275,7 @@ struct Decode {
       __syncthreads();
       pw_write_new_pair(a, he, tb, tile);
     }
-    if (wrw > 1 || kBypass || kPW) {
+    if (wrw > 1 || kBypass || kPW || kHad) {
       __syncthreads();
       // combine readout partials over row-wavefronts, add the bypass term, store o
       combine_o(a, he, tb, tile, L, wrw, flags, byp_regs, br);
@@ -1312,6 +1313,11 @@ struct Decode {
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
       float acc = L.op[j];
       for (int q = 1; q < wrw; ++q) acc += L.op[q * a.dv + j];
+      if constexpr (kHad) {
+        // the readout of the rotated state: o~, rotated back below
+        L.up[j] = acc;
+        continue;
+      }
       if (kWz) {
         if (P >= 1) {
           for (int pp = 0; pp < P; ++pp) acc += L.up[pp * a.dv + j];
@@ -1321,6 +1327,23 @@ struct Decode {
       }
       if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
+    }
+    if constexpr (kHad) {
+      // o = o~ H / g, group by group (H_jj' = (-1)^popcount(j & j') inside a group)
+      __syncthreads();
+      const int g = a.group;
+      const float ig = 1.0f / (float)g;
+      for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
+        const int base = j & ~(g - 1), jj = j & (g - 1);
+        float acc = 0.f;
+        for (int t = 0; t < g; ++t) {
+          const float v = L.up[base + t];
+          acc += (__builtin_popcount(t & jj) & 1) ? -v : v;
+        }
+        acc = __fmul_rn(acc, ig);
+        if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
+        a.o[(size_t)tile * a.dv + j] = acc;
+      }
     }
   }
 

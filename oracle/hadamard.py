@@ -15,10 +15,20 @@ Readings (the design notes list them):
       (entries +-1, unnormalised); the step rule and rounding act on y.
   H2  Dequantization inverts the rotation: x_hat = (c s) H_g / g; g is a power
       of two, so the 1/g is an exact scaling.
-  H3  Per step: x_hat_prev = dequantized state; r = fl(a_i x_hat_prev)
-      (decay); the update and the readout are those of the unquantized
-      recurrence applied to x_hat_prev (Gated DeltaNet retrieval over x_hat);
-      then y = x H_g and requantization of y.
+  H3  The step runs in the rotated basis. The rotation acts on the value
+      axis only, while the decay scales rows and the update is rank one, so
+      (A X + k w^T) H_g = A (X H_g) + k (H_g w)^T. With y_hat = fl(c s) the
+      stored (rotated) state:
+        r = fl(c fl(a_i s))                     decay, as without the rotation
+        u~ = sum_i k_i y_hat_i                  retrieval in the rotated basis
+                                                (pairwise tree of exact products)
+        u = fl(u~ H_g) / g                      Gated DeltaNet: back to the state's basis
+        w = fl(beta fl(v - fl(alpha u)))        (w = v for the other rows)
+        y = fma(k_i, fl(H_g w)_j, r_ij)         the new rotated state
+        o = (sum_i q_i y_i) H_g / g             the readout, in the state's basis
+      and y is requantized. In exact arithmetic this is the same map as
+      un-rotating, stepping and rotating again; it transforms three vectors
+      per tile instead of the whole state, twice.
   H4  The transform runs in float32 as the radix-2 butterfly with pair
       distance h = 1, 2, 4, ..., g/2 in that order, each butterfly
       (a, b) -> (fl(a + b), fl(a - b)) on positions (j, j + h), j & h = 0.
@@ -29,7 +39,7 @@ from typing import Dict
 
 import numpy as np
 
-from .fp import Arith, F32
+from .fp import Arith, F32, F64
 from .recurrence import (OState, NONFINITE, SCALE_OVERFLOW, CLIPPED, decay_rows, qrange, scale_rule,
                          quantize_group_codes, _expand, _flat, _retrieval, _group_absmax, _fp16_midpoint_near,
                          FORGIVE)
@@ -77,20 +87,25 @@ def step(st: OState, inp: Dict, w, A: Arith = F32, static=None):
     a = decay_rows(w, inp, static)
     new = st.copy()
     new.t = st.t + 1
-    xprev = dequant(st, w, A)
-    r = A.mul(a[:, :, None], xprev)
+    codes_f = st.codes.astype(A.dt)
+    s_full = _expand(st.scales, g)
+    # decay in the rotated basis: r = fl(c fl(a_i s))
+    c1 = A.mul(a[:, :, None], st.scales)
+    r = A.mul(codes_f, _expand(c1, g))
     if w.model == "gdn":
         alpha = A.c(_flat(w, inp["alpha"])).reshape(T)
         beta = A.c(_flat(w, inp["beta"])).reshape(T)
-        u = _retrieval(w, A, k, xprev)
+        yhat = A.mul(codes_f, s_full)
+        u = inverse(_retrieval(w, A, k, yhat), g, A)
         wv = A.mul(beta[:, None], A.sub(v, A.mul(alpha[:, None], u)))
     else:
         wv = v
-    x = A.c(A.fma(k[:, :, None], wv[:, None, :], r))
-    if not np.all(np.isfinite(x)):
+    y = A.c(A.fma(k[:, :, None], fwht(wv, g, A)[:, None, :], r))
+    if not np.all(np.isfinite(y)):
         new.flags |= NONFINITE
-    o = np.einsum("ti,tij->tj", q.astype(np.float64), x.astype(np.float64))
-    y = fwht(x, g, A)
+    # the readout in the state's basis: (q^T y) H / g, in float64
+    o = fwht(np.einsum("ti,tij->tj", q.astype(np.float64), y.astype(np.float64)), g, F64) / g
+    x = inverse(y, g, F64)      # the unquantized new state in its own basis (diagnostics)
     bits_full = st.bits[:, None, None]
     _, _, qmax = qrange(bits_full)
     m = _group_absmax(y, g)
@@ -113,5 +128,5 @@ def step(st: OState, inp: Dict, w, A: Arith = F32, static=None):
         gnear |= _fp16_midpoint_near(ratio) & (grew if thr is not None else True)
     near |= _expand(gnear, g)
     diag = dict(x=x, y=y, r=r, w=wv, m=m, grew=grew, thr=thr, s_new=s_new, near=near, group_near=gnear,
-                clipped=clipped, xprev=xprev)
+                clipped=clipped)
     return new, o, diag
