@@ -256,7 +256,7 @@ typedef __attribute__((address_space(1))) uint32_t g_u32;
 typedef __attribute__((address_space(1))) uint16_t g_u16;
 typedef __attribute__((address_space(1))) uint8_t g_u8;
 template <bool BF16>
-static __device__ __noinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, const void* qp, int tile, int dk, int W,
+static __device__ __forceinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, const void* qp, int tile, int dk, int W,
                                               int n, int slot, float al, float be, float* z) {
   const bool leaving = n == W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
@@ -469,7 +469,7 @@ struct Decode {
   static constexpr bool kHad = FEAT == kFeatHad;
   // pure-write window (Gated DeltaNet): the history takes the transition with v = 0
   static constexpr bool kPW = FEAT == kFeatPW;
-  static constexpr bool kDense = kF32 || kPW;
+  static constexpr bool kDense = kF32;
   // BDR needs the pre-rounding x next to the codes; so do the diagnostics
   static constexpr bool kKeepX = !kF32 && (FEAT == kFeatBdr || kYoked || kDiag);
 
@@ -675,33 +675,17 @@ struct Decode {
       load_chunk<BITS>(cp, ch);
       load_scales8(sf16, sp, s_old);
       unpack_scaled(ch, x);
-      if constexpr (kPW) {
-        // dense history fl(c s); the pair written W steps ago leaves the
-        // window and joins it before the transition: hd = fma(u_i, w_j, h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[i][j] = __fmul_rn(__fmul_rn(x[i][j], invF), s_old[i]);
-        if (a.n == a.pw) {
-          const int slot = (int)((a.t_next - 1) % a.pw);
-          const uint8_t* up = tb + he.bypass_u + (size_t)slot * a.dk + i0;
-          const uint8_t* wp = tb + he.bypass_w + (size_t)slot * a.dv + j0;
-          const uint2 ub = *reinterpret_cast<const uint2*>(up);
-          const uint2 wb = *reinterpret_cast<const uint2*>(wp);
-          float ue[8], we[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ue[e] = e4m3_to_f32((ub.x >> (8 * e)) & 0xFFu);
-            ue[e + 4] = e4m3_to_f32((ub.y >> (8 * e)) & 0xFFu);
-            we[e] = e4m3_to_f32((wb.x >> (8 * e)) & 0xFFu);
-            we[e + 4] = e4m3_to_f32((wb.y >> (8 * e)) & 0xFFu);
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[i][j] = __builtin_fmaf(ue[i], we[j], x[i][j]);
-        }
-      }
+    }
+    // the pure-write window's leaving pair (the one written W steps ago):
+    // its bytes load with the state's, it joins after the transition
+    uint2 pw_ub = make_uint2(0u, 0u), pw_wb = make_uint2(0u, 0u);
+    const bool pw_leaving = kPW && a.n == a.pw;
+    if constexpr (kPW) {
+      // loaded whether or not the pair leaves (the slot is always inside the
+      // window's sections), so no branch separates these loads from the rest
+      const int slot = (int)((a.t_next - 1) % a.pw);
+      pw_ub = *reinterpret_cast<const uint2*>(tb + he.bypass_u + (size_t)slot * a.dk + i0);
+      pw_wb = *reinterpret_cast<const uint2*>(tb + he.bypass_w + (size_t)slot * a.dv + j0);
     }
     float qf[8], kf[8], dec[8];
     load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
@@ -772,6 +756,47 @@ struct Decode {
         if constexpr (kBypass) x[i][j] = ri;
         else x[i][j] = __builtin_fmaf(kf[i], wv[j], ri);
       }
+
+    // the leaving window pair joins after the transition: its key takes the
+    // transition, u' = fl(a fl(u - fl(b k))) with b = fl(beta k^T u), and
+    // x += u' w^T. k^T u is summed in the retrieval's pairwise row order:
+    // the lane's rows, then the row lanes, then the row wavefronts.
+    if constexpr (kPW) {
+      if (pw_leaving) {
+        float ue[8], we[8], t8[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ue[e] = e4m3_to_f32((pw_ub.x >> (8 * e)) & 0xFFu);
+          ue[e + 4] = e4m3_to_f32((pw_ub.y >> (8 * e)) & 0xFFu);
+          we[e] = e4m3_to_f32((pw_wb.x >> (8 * e)) & 0xFFu);
+          we[e + 4] = e4m3_to_f32((pw_wb.y >> (8 * e)) & 0xFFu);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t8[i] = __fmul_rn(kf[i], ue[i]);
+        float d = row_lane_sum<NB>(tree8(t8));
+        if (wrw > 1) {
+          if (wc == 0 && lane == 0) L.z[wr] = d;
+          __syncthreads();
+          const float l0 = L.z[0], l1 = L.z[1];
+          if (wrw == 2) {
+            d = __fadd_rn(l0, l1);
+          } else {
+            const float a01 = __fadd_rn(l0, l1), a23 = __fadd_rn(L.z[2], L.z[3]);
+            d = wrw == 4 ? __fadd_rn(a01, a23)
+                         : __fadd_rn(__fadd_rn(a01, a23),
+                                     __fadd_rn(__fadd_rn(L.z[4], L.z[5]), __fadd_rn(L.z[6], L.z[7])));
+          }
+          __syncthreads();
+        }
+        const float b = __fmul_rn(dwp.be, d);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float u2 = __fmul_rn(dwp.al, __fsub_rn(ue[i], __fmul_rn(b, kf[i])));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[i][j] = __builtin_fmaf(u2, we[j], x[i][j]);
+        }
+      }
+    }
 
     // readout partial o_j over this wavefront's rows
     {

@@ -152,6 +152,18 @@ __device__ __forceinline__ void xtree(float v[8], int lane) {
   if constexpr (NB >= 4) v[0] = __fadd_rn(v[0], swz_xor(v[0], 4));
 }
 
+// Sum of one value per row lane over the NB row-lane bits, in the order of
+// xtree (lane bit 5 first, which carries the lowest row-block bit): the
+// pairwise row order of the retrieval. Every lane gets the sum.
+template <int NB>
+__device__ __forceinline__ float row_lane_sum(float d) {
+  d = __fadd_rn(d, __shfl_xor(d, 32, 64));
+  if constexpr (NB >= 2) d = __fadd_rn(d, __shfl_xor(d, 16, 64));
+  if constexpr (NB >= 3) d = __fadd_rn(d, dpp_ror8(d));
+  if constexpr (NB >= 4) d = __fadd_rn(d, swz_xor(d, 4));
+  return d;
+}
+
 // Column (0..7, inside the lane's column block) held in slot s after xtree.
 template <int NB>
 __device__ __forceinline__ int xtree_col(int s, int lane) {

@@ -19,12 +19,17 @@ Readings (the design notes list them):
   W2  A pair that stays in the window takes the transition:
         d = pairwise sum over i (row order) of fl(k_i u_i), b = fl(beta d),
         u_i <- fp8(fl(alpha fl(u_i - fl(b k_i)))).
-  W3  At step t > W the pair written at step t - W leaves: it is added to the
-      dequantized history before the transition, hd = fma(u_i, w_j, fl(c s)),
-      and the history takes the transition alone, which is the GDN step with
-      v = 0: r = fl(alpha hd), g_j = pairwise sum over i of fl(k_i hd_ij),
-      w_j = fl(beta fl(0 - fl(alpha g_j))), x = fma(k_i, w_j, r). x is then
-      requantized by the history's scale rule.
+  W3  At step t > W the pair written at step t - W leaves and joins the
+      history. The transition T(S) = alpha (S - beta k (k^T S)) is linear, so
+      T(H + u w^T) = T(H) + T(u) w^T: the history and the leaving pair take
+      the transition separately and the pair is added after it. The history
+      takes the GDN step with v = 0 on y_hat = fl(c s), as a state without a
+      window does: r = fl(c fl(alpha s)), g_j = pairwise sum over i of
+      fl(k_i y_hat_ij) (exact products), w_j = fl(beta fl(0 - fl(alpha g_j))),
+      x = fma(k_i, w_j, r). The leaving pair's key takes the W2 transition
+      without the FP8 rounding, u'_i = fl(alpha fl(u_i - fl(b k_i))), and
+      joins: x = fma(u'_i, w_leave_j, x). x is then requantized by the
+      history's scale rule. (An fp32 history uses r = fl(alpha S).)
   W4  The new pair takes the slot the leaving pair freed (or the next empty
       slot while the window fills).
   W5  o_t = x^T q + sum_c w_c (u_c^T q) over the window after the step.
@@ -129,17 +134,24 @@ def step(st: OState, inp: Dict, w, A: Arith = F32, static=None, rounding=True):
     n = min(st.t, W)
     slot = st.t % W
     leaving = st.t >= W
-    # history, dequantized (+ the leaving pair), then the transition with v = 0 (W3)
+    # the history takes the transition with v = 0 (W3)
     if st.S32 is not None:
         H = A.c(st.S32)
+        r = A.mul(alpha[:, None, None], H)
     else:
-        H = A.mul(st.codes.astype(A.dt), _expand(st.scales, g))
-    if leaving:
-        H = A.c(A.fma(st.U[:, :, slot][:, :, None], st.W[:, :, slot][:, None, :], H))
-    r = A.mul(alpha[:, None, None], H)
+        codes_f = st.codes.astype(A.dt)
+        H = A.mul(codes_f, _expand(st.scales, g))
+        r = A.mul(codes_f, _expand(A.mul(alpha[:, None, None], st.scales), g))
     gsum = _retrieval(w, A, k, H)
     wv = A.mul(beta[:, None], A.sub(A.c(0.0), A.mul(alpha[:, None], gsum)))
     x = A.c(A.fma(k[:, :, None], wv[:, None, :], r))
+    # the leaving pair: its key takes the transition (W2 without FP8) and joins (W3)
+    if leaving:
+        u = A.c(st.U[:, :, slot])
+        d = pairwise_sum(A.mul(k, u), 1, A.add) if A.name == "f32" else np.sum(k * u, axis=1)
+        b = A.mul(beta, d)
+        up = A.mul(alpha[:, None], A.sub(u, A.mul(b[:, None], k)))
+        x = A.c(A.fma(up[:, :, None], st.W[:, :, slot][:, None, :], x))
     if not np.all(np.isfinite(x)):
         new.flags |= NONFINITE
     # window pairs that stay take the transition (W2)
