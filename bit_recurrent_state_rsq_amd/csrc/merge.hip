@@ -39,7 +39,7 @@ namespace rsq {
 constexpr int kMergeItersWide = 5;    // p >= 4k + 4
 constexpr int kMergeItersNarrow = 12;
 constexpr int kJacobiSweeps = 12;  // upper bound; stops once the off-diagonal part is negligible
-constexpr int kChunkCols = 8;      // basis columns per cross-wavefront reduction pass
+constexpr int kChunkMin = 8, kChunkMax = 32;   // basis columns per cross-wavefront reduction pass
 constexpr int kSm = kMaxCap + 1;   // row stride of the small p x p matrices
 // misc block layout (floats)
 constexpr int kMiscDinv = 0, kMiscOrder = kMaxCap, kMiscSroot = 2 * kMaxCap, kMiscFlag = 3 * kMaxCap,
@@ -50,7 +50,7 @@ constexpr int kMiscDinv = 0, kMiscOrder = kMaxCap, kMiscSroot = 2 * kMaxCap, kMi
 struct MergeLds {
   float* zt;    // [cap][zs]       right basis, column c at zt + c * zs
   float* yt;    // [cap][ys]       left basis
-  float* part;  // [stripes][kChunkCols][rows]  per-wavefront-stripe partial sums
+  float* part;  // [stripes][chunk][rows]  per-wavefront-stripe partial sums
   float* g;     // [kMaxCap][kSm]  Gram matrix / Cholesky factor
   float* h0;    // [kMaxCap][kSm]  Jacobi: H, double buffered
   float* h1;
@@ -66,14 +66,14 @@ __host__ __device__ inline int merge_ys(int dk) { return dk + 4; }
 constexpr int kTri = kMaxCap * (kMaxCap + 1) / 2;   // entries of a symmetric kMaxCap x kMaxCap matrix
 
 // floats of the partial-sum area: product stripes, or per-wavefront Gram partials
-__host__ __device__ inline size_t merge_part_floats(int dk, int dv, int wrw, int wcw) {
-  const size_t prod = (size_t)kChunkCols * (size_t)(wcw * dk > wrw * dv ? wcw * dk : wrw * dv);
+__host__ __device__ inline size_t merge_part_floats(int dk, int dv, int wrw, int wcw, int chunk) {
+  const size_t prod = (size_t)chunk * (size_t)(wcw * dk > wrw * dv ? wcw * dk : wrw * dv);
   const size_t gram = (size_t)wrw * wcw * kTri;
   return prod > gram ? prod : gram;
 }
 
-size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap) {
-  const size_t part = merge_part_floats(dk, dv, wrw, wcw);
+size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int chunk) {
+  const size_t part = merge_part_floats(dk, dv, wrw, wcw, chunk);
   return (size_t)cap * merge_zs(dv) + (size_t)cap * merge_ys(dk) + part + 5 * kMaxCap * kSm + kMiscFloats;
 }
 
@@ -296,8 +296,9 @@ struct Merge {
   // yt[c][i] = sum_j R_ij zt[c][j] for c < p
   static __device__ __forceinline__ void prod_rz(const StepArgs& a, const Geo& g, const float R[8][8], const MergeLds& S, int p) {
     const int zs = merge_zs(a.dv), ys = merge_ys(a.dk);
-    for (int c0 = 0; c0 < p; c0 += kChunkCols) {
-      const int nc = min(kChunkCols, p - c0);
+    const int C = a.merge_chunk;
+    for (int c0 = 0; c0 < p; c0 += C) {
+      const int nc = min(C, p - c0);
       for (int cc = 0; cc < nc; ++cc) {
         float z8[8];
         loadf8(S.zt + (size_t)(c0 + cc) * zs + g.j0, z8);
@@ -309,13 +310,13 @@ struct Merge {
           for (int j = 1; j < 8; ++j) acc = __builtin_fmaf(R[i][j], z8[j], acc);
           y8[i] = col_lane_sum<CL>(acc);
         }
-        if (g.lc == 0) storef8(S.part + ((size_t)g.wc * kChunkCols + cc) * a.dk + g.i0, y8);
+        if (g.lc == 0) storef8(S.part + ((size_t)g.wc * C + cc) * a.dk + g.i0, y8);
       }
       __syncthreads();
       for (int e = threadIdx.x; e < nc * a.dk; e += blockDim.x) {
         const int cc = e / a.dk, i = e - cc * a.dk;
         float s = S.part[(size_t)cc * a.dk + i];
-        for (int w = 1; w < g.wcw; ++w) s = __fadd_rn(s, S.part[((size_t)w * kChunkCols + cc) * a.dk + i]);
+        for (int w = 1; w < g.wcw; ++w) s = __fadd_rn(s, S.part[((size_t)w * C + cc) * a.dk + i]);
         S.yt[(size_t)(c0 + cc) * ys + i] = s;
       }
       __syncthreads();
@@ -326,8 +327,9 @@ struct Merge {
   static __device__ __forceinline__ void prod_rty(const StepArgs& a, const Geo& g, const float R[8][8], const MergeLds& S, int p) {
     const int zs = merge_zs(a.dv), ys = merge_ys(a.dk);
     const bool writer = NB < 4 || ((g.lane >> 2) & 1) == 0;
-    for (int c0 = 0; c0 < p; c0 += kChunkCols) {
-      const int nc = min(kChunkCols, p - c0);
+    const int C = a.merge_chunk;
+    for (int c0 = 0; c0 < p; c0 += C) {
+      const int nc = min(C, p - c0);
       for (int cc = 0; cc < nc; ++cc) {
         float q8[8];
         loadf8(S.yt + (size_t)(c0 + cc) * ys + g.i0, q8);
@@ -342,13 +344,13 @@ struct Merge {
         xtree<NB>(z8, g.lane);
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s)
-          if (writer) S.part[((size_t)g.wr * kChunkCols + cc) * a.dv + g.j0 + xtree_col<NB>(s, g.lane)] = z8[s];
+          if (writer) S.part[((size_t)g.wr * C + cc) * a.dv + g.j0 + xtree_col<NB>(s, g.lane)] = z8[s];
       }
       __syncthreads();
       for (int e = threadIdx.x; e < nc * a.dv; e += blockDim.x) {
         const int cc = e / a.dv, j = e - cc * a.dv;
         float s = S.part[(size_t)cc * a.dv + j];
-        for (int w = 1; w < g.wrw; ++w) s = __fadd_rn(s, S.part[((size_t)w * kChunkCols + cc) * a.dv + j]);
+        for (int w = 1; w < g.wrw; ++w) s = __fadd_rn(s, S.part[((size_t)w * C + cc) * a.dv + j]);
         S.zt[(size_t)(c0 + cc) * zs + j] = s;
       }
       __syncthreads();
@@ -573,7 +575,7 @@ struct Merge {
     S.zt = lds;
     S.yt = S.zt + (size_t)a.cap * merge_zs(a.dv);
     S.part = S.yt + (size_t)a.cap * merge_ys(a.dk);
-    S.g = S.part + merge_part_floats(a.dk, a.dv, g.wrw, g.wcw);
+    S.g = S.part + merge_part_floats(a.dk, a.dv, g.wrw, g.wcw, a.merge_chunk);
     S.h0 = S.g + kMaxCap * kSm;
     S.h1 = S.h0 + kMaxCap * kSm;
     S.v0 = S.h1 + kMaxCap * kSm;

@@ -51,6 +51,7 @@ struct Geometry {
   int cl, wr, wc, wrw, wcw, threads;
   size_t lds;         // decode / readout
   size_t lds_merge;   // bypass merge (0 without a bypass)
+  int merge_chunk;    // basis columns per merge product pass
 };
 
 constexpr size_t kLdsBytes = 160 * 1024;   // LDS of one gfx950 compute unit
@@ -175,7 +176,18 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   // per-wave w broadcast, 2 x retrieval partials, readout partials, bypass projections
   G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64)) *
           sizeof(float);
-  G.lds_merge = p.bypass ? rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap) * sizeof(float) : 0;
+  // the merge reduces its products over as many basis columns per pass as
+  // the LDS holds (fewer passes, fewer barriers); at least 8
+  G.merge_chunk = 8;
+  G.lds_merge = p.bypass ? rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap, 8) * sizeof(float) : 0;
+  if (p.bypass) {
+    for (int ch = 16; ch <= 32 && ch - 8 < p.cap; ch += 8) {
+      const size_t b = rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap, ch) * sizeof(float);
+      if (b > kLdsBytes) break;
+      G.merge_chunk = ch;
+      G.lds_merge = b;
+    }
+  }
   if (G.lds_merge > kLdsBytes)
     return fail(RSQ_E_UNSUPPORTED, "the bypass merge of a %d x %d tile with %d columns needs %zu bytes of LDS",
                 c->d_k, c->d_v, p.cap, G.lds_merge);
@@ -271,6 +283,7 @@ StepArgs base_args(rsq_state* st) {
   a.scale_f16 = st->cfg.scale_dtype == RSQ_F16;
   a.hadamard = st->cfg.hadamard;
   a.pw = st->pw;
+  a.merge_chunk = st->geo.merge_chunk;
   a.uniform = st->uniform ? 1 : 0;
   if (st->uniform) {
     a.uni = st->heads[0];

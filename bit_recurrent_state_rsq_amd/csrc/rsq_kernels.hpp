@@ -49,6 +49,9 @@ struct StepArgs {
   int32_t uniform;
   uint64_t uni_stride;
   HeadEntry uni;
+  // bypass merge: basis columns per product pass (the host takes the
+  // largest of 8, 16, 24, 32 whose partial sums fit the LDS)
+  int32_t merge_chunk;
 };
 
 // Head table entry of head h.
@@ -66,8 +69,9 @@ DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
 DecodeFn readout_kernel_for(int cl);
 DecodeFn merge_kernel_for(int cl);
 // dynamic LDS (floats) of the merge kernel for a tile of d_k x d_v split into
-// wrw x wcw wavefronts with `cap` bypass columns
-size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap);
+// wrw x wcw wavefronts with `cap` bypass columns, reducing products over
+// `chunk` basis columns per pass
+size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int chunk);
 
 // Decay of key row i of a tile (Table 1, A_t column).
 __device__ __forceinline__ float row_decay(const StepArgs& a, const HeadEntry& he, int model,
