@@ -373,6 +373,18 @@ struct Merge {
       const float* xb = xt + (size_t)cb * xs;
       float s0 = 0.f, s1 = 0.f;
       int r = r0;
+      if ((rows & 3) == 0) {
+        // 16-byte reads: the row stride and the wavefront's first row are
+        // multiples of 4 floats
+        for (; r + 3 < r1; r += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(xa + r);
+          const float4 b4 = *reinterpret_cast<const float4*>(xb + r);
+          s0 = __builtin_fmaf(a4.x, b4.x, s0);
+          s1 = __builtin_fmaf(a4.y, b4.y, s1);
+          s0 = __builtin_fmaf(a4.z, b4.z, s0);
+          s1 = __builtin_fmaf(a4.w, b4.w, s1);
+        }
+      }
       for (; r + 1 < r1; r += 2) {
         s0 = __builtin_fmaf(xa[r], xb[r], s0);
         s1 = __builtin_fmaf(xa[r + 1], xb[r + 1], s1);
@@ -438,10 +450,11 @@ struct Merge {
     for (int pass = 0; pass < passes; ++pass) {
       gram(g, xt, xs, m, p, S.g, S.part);
       if (g.wave == 0) {
-        // p rounded up to a multiple of 8 fixes the loop bounds; the padded
-        // columns are zero and drop out like any dependent column
+        // p rounded up to a multiple of 4 or 8 fixes the loop bounds; the
+        // padded columns are zero and drop out like any dependent column
         if (p <= 8) cholesky<8>(g.lane, p, S.g, dinv, lt);
         else if (p <= 16) cholesky<16>(g.lane, p, S.g, dinv, lt);
+        else if (p <= 20) cholesky<20>(g.lane, p, S.g, dinv, lt);
         else if (p <= 24) cholesky<24>(g.lane, p, S.g, dinv, lt);
         else cholesky<32>(g.lane, p, S.g, dinv, lt);
       }
