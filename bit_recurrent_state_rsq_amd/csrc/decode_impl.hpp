@@ -1359,11 +1359,22 @@ struct Decode {
       const int g = a.group;
       const float ig = 1.0f / (float)g;
       for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
-        const int base = j & ~(g - 1), jj = j & (g - 1);
-        float acc = 0.f;
-        for (int t = 0; t < g; ++t) {
-          const float v = L.up[base + t];
-          acc += (__builtin_popcount(t & jj) & 1) ? -v : v;
+        float acc;
+        if (g <= 64) {
+          // the butterflies of the fast transform, across the lanes of a
+          // group (groups are aligned, so a lane's partners are all live)
+          acc = L.up[j];
+          for (int m = 1; m < g; m <<= 1) {
+            const float o = __shfl_xor(acc, m, 64);
+            acc = (j & m) ? __fsub_rn(o, acc) : __fadd_rn(acc, o);
+          }
+        } else {
+          const int base = j & ~(g - 1), jj = j & (g - 1);
+          acc = 0.f;
+          for (int t = 0; t < g; ++t) {
+            const float v = L.up[base + t];
+            acc += (__builtin_popcount(t & jj) & 1) ? -v : v;
+          }
         }
         acc = __fmul_rn(acc, ig);
         if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
