@@ -108,11 +108,12 @@ enum {
  *                  abstract). The state is the low-bit history H plus the last
  *                  W writes as FP8 (OCP E4M3, saturating) pairs (u, w) =
  *                  (k_t, beta_t v_t), slot (t - 1) mod W. Each step the pairs
- *                  that stay take the transition u <- alpha (u - beta k (k^T u)),
- *                  the pair written W steps earlier is added to H, and H takes
- *                  the transition alone (the delta-rule step with v = 0) before
- *                  requantization; o_t = x^T q + sum_c w_c (u_c^T q). Quantized
- *                  widths with dynamic or persistent scales only
+ *                  that stay take the transition u <- alpha (u - beta k (k^T u)).
+ *                  H takes it alone (the delta-rule step with v = 0); the pair
+ *                  written W steps earlier takes it too, unrounded, and joins
+ *                  H after it, x = H' + u' w^T, before requantization. Then
+ *                  o_t = x^T q + sum_c w_c (u_c^T q). Quantized widths with
+ *                  dynamic or persistent scales only
  *
  * Supported shapes (others return RSQ_E_UNSUPPORTED): d_v a multiple of
  * 8 * max(4, group / 8); d_k a multiple of 512 / max(4, group / 8) rows per
