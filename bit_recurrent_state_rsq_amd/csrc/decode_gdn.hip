@@ -3,4 +3,5 @@
 
 namespace rsq {
 DecodeFn decode_gdn(int cl, int feat, int spec) { return decode_pick_cl<kGDN>(cl, feat, spec); }
+DecodeFn decode_boost_twin(DecodeFn fn) { return decode_pick_boost<kGDN, 4>(fn); }
 }  // namespace rsq

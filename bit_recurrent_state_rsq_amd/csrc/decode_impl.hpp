@@ -645,7 +645,7 @@ struct Decode {
     return in_elem(SP::bf16(a), a.v, (size_t)tile * a.dv + j);
   }
 
-  template <int BITS>
+  template <int BITS, bool BOOST = false>
   static __device__ __forceinline__ void body(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                               const Lds& L, uint32_t& flags) {
     const bool bf16 = SP::bf16(a), sf16 = SP::sf16(a);
@@ -700,6 +700,8 @@ struct Decode {
     // in the BDR, yoked and accounting variants, which already run at the
     // register limit)
     if constexpr (!(FEAT == kFeatBdr || kYoked || kDiag)) __builtin_amdgcn_sched_barrier(0);
+    // the loads are out: back to the normal issue priority
+    if constexpr (BOOST) __builtin_amdgcn_s_setprio(0);
 
     // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
     // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
@@ -1254,7 +1256,12 @@ struct Decode {
       W[j] = (uint8_t)f32_to_e4m3(__fmul_rn(be, in_elem(bf16, a.v, (size_t)tile * a.dv + j)));
   }
 
+  // BOOST: every wavefront of the grid is resident from the start (the host
+  // checks), and the ones still issuing their loads go ahead of those already
+  // computing. With several rounds of workgroups this measured slower.
+  template <bool BOOST = false>
   static __device__ void run(const StepArgs& a) {
+    if constexpr (BOOST) __builtin_amdgcn_s_setprio(3);
     extern __shared__ float lds[];
     const int tile = blockIdx.x;
     const int bb = tile / a.H, h = tile - bb * a.H;
@@ -1280,12 +1287,12 @@ struct Decode {
     }
 
     if constexpr (kF32) {
-      body<32>(a, he, tb, tile, L, flags);
+      body<32, BOOST>(a, he, tb, tile, L, flags);
     } else {
       switch (he.bits) {
-        case 4: body<4>(a, he, tb, tile, L, flags); break;
-        case 6: body<6>(a, he, tb, tile, L, flags); break;
-        default: body<8>(a, he, tb, tile, L, flags); break;
+        case 4: body<4, BOOST>(a, he, tb, tile, L, flags); break;
+        case 6: body<6, BOOST>(a, he, tb, tile, L, flags); break;
+        default: body<8, BOOST>(a, he, tb, tile, L, flags); break;
       }
     }
     if constexpr (kBypass) {
@@ -1403,9 +1410,21 @@ __global__ __launch_bounds__(512) void decode_kernel(StepArgs a) {
 }
 
 // specialised steps held to at most 128 VGPRs: four wavefronts per SIMD
-template <int MODEL, int CL, int FEAT, int SPEC>
+template <int MODEL, int CL, int FEAT, int SPEC, bool BOOST = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel_occ(StepArgs a) {
-  Decode<MODEL, CL, FEAT, SPEC>::run(a);
+  Decode<MODEL, CL, FEAT, SPEC>::template run<BOOST>(a);
+}
+
+// The raised-priority twin of a decode kernel, for launches whose grid is
+// resident at once, or nullptr. Only the plain Gated DeltaNet step with
+// binary16 persistent steps has one (measured on its 64 x 16 head workload).
+template <int MODEL, int CL>
+DecodeFn decode_pick_boost(DecodeFn fn) {
+  if constexpr (MODEL == kGDN && CL == 4) {
+    if (fn == decode_kernel_occ<MODEL, CL, kFeatPlain, kSpecPersF16Bf16G32>)
+      return decode_kernel_occ<MODEL, CL, kFeatPlain, kSpecPersF16Bf16G32, true>;
+  }
+  return nullptr;
 }
 
 template <int MODEL, int CL, int SPEC>

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <mutex>
 #include <map>
+#include <tuple>
 #include <string>
 #include <utility>
 #include <vector>
@@ -292,10 +293,37 @@ StepArgs base_args(rsq_state* st) {
   return a;
 }
 
+// Whether all `blocks` workgroups of fn are resident on the current device at
+// once (occupancy per CU times the CU count), cached per device, kernel, block
+// size and LDS size. A failed query answers no.
+bool one_round(rsq::DecodeFn fn, unsigned blocks, unsigned threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, unsigned, size_t>, long> resident;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(fn), threads, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = resident.find(key);
+  if (it == resident.end()) {
+    int per_cu = 0, cus = 0;
+    long n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), (int)threads, lds) ==
+            hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n = (long)per_cu * cus;
+    (void)hipGetLastError();   // a failed query leaves no error for the launch to report
+    it = resident.emplace(key, n).first;
+  }
+  return (long)blocks <= it->second;
+}
+
 rsq_status launch(rsq::DecodeFn fn, const rsq_state* st, const StepArgs& a, void* stream,
                   void* ev_start = nullptr, void* ev_stop = nullptr, size_t lds = 0) {
   const dim3 grid(st->cfg.batch * st->cfg.heads), block(st->geo.threads);
   if (lds == 0) lds = st->geo.lds;
+  // a grid resident at once runs the raised-priority twin, where there is one
+  if (rsq::DecodeFn twin = rsq::decode_boost_twin(fn))
+    if (one_round(fn, grid.x, block.x, lds)) fn = twin;
   if (lds > 64 * 1024) {
     // raised once per kernel and device, to the largest size a launch has
     // asked for (the attribute call is host work that need not repeat every step)

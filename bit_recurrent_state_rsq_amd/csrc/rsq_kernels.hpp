@@ -66,6 +66,8 @@ __device__ __forceinline__ HeadEntry head_entry(const StepArgs& a, int h) {
 
 typedef void (*DecodeFn)(StepArgs);
 DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
+// the raised-priority twin of a decode kernel for grids resident at once, or nullptr
+DecodeFn decode_boost_twin(DecodeFn fn);
 DecodeFn readout_kernel_for(int cl);
 DecodeFn merge_kernel_for(int cl);
 // dynamic LDS (floats) of the merge kernel for a tile of d_k x d_v split into
