@@ -1416,13 +1416,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void d
 }
 
 // The raised-priority twin of a decode kernel, for launches whose grid is
-// resident at once, or nullptr. Only the plain Gated DeltaNet step with
-// binary16 persistent steps has one (measured on its 64 x 16 head workload).
+// resident at once, or nullptr. Only the plain and rotated Gated DeltaNet
+// steps with binary16 persistent steps have one (measured on the 64 x 16 head
+// workload; the windowed step gained nothing).
 template <int MODEL, int CL>
 DecodeFn decode_pick_boost(DecodeFn fn) {
   if constexpr (MODEL == kGDN && CL == 4) {
     if (fn == decode_kernel_occ<MODEL, CL, kFeatPlain, kSpecPersF16Bf16G32>)
       return decode_kernel_occ<MODEL, CL, kFeatPlain, kSpecPersF16Bf16G32, true>;
+    if (fn == decode_kernel_occ<MODEL, CL, kFeatHad, kSpecPersF16Bf16G32>)
+      return decode_kernel_occ<MODEL, CL, kFeatHad, kSpecPersF16Bf16G32, true>;
   }
   return nullptr;
 }
