@@ -12,7 +12,11 @@ vectorized oracle shows up as a disagreement:
                  Updates in Low-Bit Recurrent State Quantization": BDR moves a
                  reversed element to the update's side)
   step_tile      one decode step of one tile with scalar arithmetic, in the
-                 same fp32 chain as the vectorized oracle (or float64)
+                 same fp32 chain as the vectorized oracle (or float64); with
+                 bypass columns (U, W) it also runs the bypass side of the
+                 step: for Gated DeltaNet the retrieval reads s_hat + U W^T,
+                 every update goes to a new fp16 column pair and the state
+                 only decays
 """
 from fractions import Fraction
 import math
@@ -71,13 +75,19 @@ def _round_half_even(y):
     return fl if fl % 2 == 0 else fl + 1
 
 
+def _f16(x):
+    return float(np.float16(x))
+
+
 def step_tile(codes, scales, bits, a, q, k, v, model, group, scale_mode,
               scale_dtype, trigger=1.0, alpha=None, beta=None, bdr=False,
-              bdr_eps=0.5, mode="f32"):
+              bdr_eps=0.5, mode="f32", U=None, W=None):
     """One decode step of one tile with scalar loops.
 
     codes [d_k][d_v] ints, scales [d_k][d_v/group] floats, a [d_k] row decays,
-    q, k [d_k], v [d_v]. Returns (codes, scales, o list, x matrix).
+    q, k [d_k], v [d_v]. Returns (codes, scales, o list, x matrix); with a
+    bypass, U and W are lists of columns (U[c][i], W[c][j], binary16 values)
+    and the new U, W are returned after x.
     """
     dk, dv = len(codes), len(codes[0])
     ng = dv // group
@@ -103,11 +113,23 @@ def step_tile(codes, scales, bits, a, q, k, v, model, group, scale_mode,
             return float(np.float16(x))
         return float(np.float32(x))
 
+    bypass = U is not None
+    n = len(U) if bypass else 0
     wv = [v[j] for j in range(dv)]
     if model == "gdn":
+        # the bypass's projections of k: z_c = sum_i U_ic k_i
+        zk = []
+        for c in range(n):
+            terms = [mul(U[c][i], k[i]) for i in range(dk)]
+            zk.append(_pairwise(terms, add) if mode == "f32" else math.fsum(terms))
         for j in range(dv):
             terms = [mul(k[i], mul(codes[i][j], scales[i][j // group])) for i in range(dk)]
             u = _pairwise(terms, add) if mode == "f32" else math.fsum(terms)
+            if n:
+                b = F(0.0)
+                for c in range(n):
+                    b = fma(W[c][j], zk[c], b)
+                u = add(u, b)
             wv[j] = mul(beta, sub(v[j], mul(alpha, u)))
     x = [[None] * dv for _ in range(dk)]
     r = [[None] * dv for _ in range(dk)]
@@ -115,8 +137,18 @@ def step_tile(codes, scales, bits, a, q, k, v, model, group, scale_mode,
         for j in range(dv):
             c1 = mul(a[i], scales[i][j // group])
             r[i][j] = mul(codes[i][j], c1)
-            x[i][j] = fma(k[i], wv[j], r[i][j])
+            x[i][j] = r[i][j] if bypass else fma(k[i], wv[j], r[i][j])
     o = [sum(float(q[i]) * float(x[i][j]) for i in range(dk)) for j in range(dv)]
+    if bypass:
+        # decay the held columns (the exact product rounded once to binary16),
+        # append the update as a new column pair, read the bypass out
+        U2 = [[_f16(float(a[i]) * float(U[c][i])) for i in range(dk)] for c in range(n)]
+        W2 = [list(W[c]) for c in range(n)]
+        U2.append([_f16(k[i]) for i in range(dk)])
+        W2.append([_f16(wv[j]) for j in range(dv)])
+        for j in range(dv):
+            o[j] += sum(float(W2[c][j]) * sum(float(U2[c][i]) * float(q[i]) for i in range(dk))
+                        for c in range(n + 1))
     new_codes = [[0] * dv for _ in range(dk)]
     new_scales = [[0.0] * ng for _ in range(dk)]
     for i in range(dk):
@@ -140,7 +172,7 @@ def step_tile(codes, scales, bits, a, q, k, v, model, group, scale_mode,
                     else:
                         y = float(x[i][j]) / s_new
                     c = min(max(_round_half_even(y), lo), hi)
-                if bdr and s_new != 0:
+                if bdr and s_new != 0 and not bypass:
                     sg = int(np.sign(k[i]) * np.sign(wv[j]))
                     if sg != 0:
                         val = float(mul(c, s_new))
@@ -150,4 +182,6 @@ def step_tile(codes, scales, bits, a, q, k, v, model, group, scale_mode,
                             if err <= float(mul(add(0.5, bdr_eps), s_new)):
                                 c = cand
                 new_codes[i][j] = c
+    if bypass:
+        return new_codes, new_scales, o, x, U2, W2
     return new_codes, new_scales, o, x

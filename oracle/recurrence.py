@@ -56,6 +56,17 @@ notes of the repository):
         s' from fl(m / qmax) (correctly rounded), then the storage dtype
         inv = RN(1/s'); y = x inv (exact); c = clamp(RNE(y))
       The readout o_t is compared with a tolerance, so its order is free.
+  R10 Gated DeltaNet with a bypass: the state read by the retrieval is the
+      stored state plus the bypass, S_{t-1} = s_hat + U W^T, so
+      u = s_hat^T k + W (U^T k). U and W are the factors before this step's
+      decay and append. In mode 'f32' each term keeps R9's rules:
+        u~_j = pairwise sum over i of fl(k_i s_hat_ij)         (R9)
+        z_c  = pairwise sum over i of fl(U_ic k_i)             (the same tree)
+        b_j  = W_j0 z_0 + W_j1 z_1 + ... in column order, one fused
+               multiply-add per column, from 0
+        u_j  = fl(u~_j + b_j)
+      then w_j = fl(beta fl(v_j - fl(alpha u_j))) as without a bypass. The
+      whole update k w^T goes into the bypass (R8).
 """
 from dataclasses import dataclass, field, replace
 from typing import Dict, Optional, Tuple
@@ -290,6 +301,20 @@ def _retrieval(w, A, k, shat_or_S):
     return A.tree_sum(terms, axis=1)
 
 
+def _bypass_retrieval(A, k, U, W):
+    """The bypass's share of the Gated DeltaNet retrieval, b = W (U^T k) (R10).
+
+    k [T, d_k]; U [T, d_k, n], W [T, d_v, n] (binary16 values). Returns b [T, d_v]:
+    z_c = pairwise sum over rows of fl(U_ic k_i), then b_j accumulated over the
+    columns in order with one fused multiply-add each.
+    """
+    z = A.tree_sum(A.mul(U, k[:, :, None]), axis=1)          # [T, n]
+    b = A.c(np.zeros(W.shape[:2]))
+    for c in range(U.shape[2]):
+        b = A.c(A.fma(W[:, :, c], z[:, c][:, None], b))
+    return b
+
+
 def step(st: OState, inp: Dict, w, A: Arith = F32, static=None):
     """One decode step of every tile (Table 1 + R1-R9).
 
@@ -333,10 +358,10 @@ def step(st: OState, inp: Dict, w, A: Arith = F32, static=None):
     r = A.mul(codes_f, _expand(c1, g))
     # 2. retrieval (GDN): w = beta (v - alpha * S^T k)
     if gdn:
-        if st.U is not None and st.n > 0:
-            raise NotImplementedError("bypass with the delta rule is not part of this oracle")
         shat = A.mul(codes_f, s_full)
         u = _retrieval(w, A, k, shat)
+        if st.U is not None and st.n > 0:
+            u = A.add(u, _bypass_retrieval(A, k, st.U[:, :, :st.n], st.W[:, :, :st.n]))
         wv = A.mul(beta[:, None], A.sub(v, A.mul(alpha[:, None], u)))
         diag["u"] = u
     else:
@@ -428,7 +453,7 @@ def merge(st: OState, w, A: Arith = F32):
     for ti in range(T):
         Uu, S, Vt = np.linalg.svd(R[ti], full_matrices=False)
         svals[ti] = S
-        for j in range(k):
+        for j in range(min(k, S.size)):       # rank <= min(d_k, d_v): further columns stay 0
             uc = f16_round(Uu[:, j] * np.sqrt(S[j]))
             wc = f16_round(Vt[j, :] * np.sqrt(S[j]))
             # sign fixed on the stored column (binary16 rounding is odd-symmetric)

@@ -41,8 +41,39 @@ def test_table9_bits(row):
         # 6.76 is printed for k+m = 24 where the formula gives 6.75
         assert abs(peak - peak_p) <= (0.0101 if km == 24 else 0.005 + 1e-12)
     else:
-        # GLA's printed bits sit 0.06 above this shape's formula (unexplained by the page)
-        assert 0 < avg_p - avg < 0.07 and 0 < peak_p - peak < 0.07
+        # GLA's printed bits sit 0.06-0.07 above this shape's formula; see
+        # test_gla_bits_fit_no_head_shape for why the GLA row stays unpinned
+        assert 0.055 < avg_p - avg < 0.07 and 0.055 < peak_p - peak < 0.075
+
+
+def test_gla_bits_fit_no_head_shape():
+    """The GLA entries of Table 6 (k = 1, m = 15: 5.31 / 6.07) and Table 9
+    (k + m = 8: 4.94 / 5.31) are not reproduced by the storage formula
+    4 bits + scale bits / g + n * 16 (d_k + d_v) / (d_k d_v) at any head shape,
+    group size or scale width: the four values need a slope per bypass column
+    and an intercept that no (d_k, d_v, g, scale bits) gives together. They sit
+    0.06-0.07 bits above the GDN entries at the same k and m, as if a GLA head
+    stored something more than its codes, step sizes and fp16 bypass columns,
+    which the page does not describe. The GLA storage bits are therefore
+    parity unpinned; GDN, RetNet (Tables 6, 8, 9) and Mamba2 (Table 6) are
+    pinned above."""
+    t6, t9 = GOLD["table6"]["GLA"], [r for r in GOLD["table9"]["rows"] if r[0] == "GLA"][0]
+    want = [(1 + (t6["m"] - 1) / 2, t6["avg"]), (1 + t6["m"], t6["peak"]),
+            (1 + (t9[1] - 2) / 2, t9[2]), (t9[1], t9[3])]
+    sizes = [16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024, 2048, 4096]
+    fits = []
+    for dk in sizes:
+        for dv in sizes:
+            for g in (8, 16, 32, 64, 128, 256):
+                for sb in (8, 16, 32):
+                    rho = (dk + dv) / (dk * dv)
+                    if all(abs(4 + sb / g + n * 16 * rho - v) <= 0.005 + 1e-9 for n, v in want):
+                        fits.append((dk, dv, g, sb))
+    assert fits == []
+    # while the GDN entries at the same k, m fit the reading's shape
+    gdn = GOLD["table6"]["GDN"]
+    avg, peak = acc.bits_per_element(4, 32, 16, *GDN_SHAPE, k=gdn["k"], m=gdn["m"])
+    assert (round(avg, 2), round(peak, 2)) == (gdn["avg"], gdn["peak"])
 
 
 def test_table6_bits():
