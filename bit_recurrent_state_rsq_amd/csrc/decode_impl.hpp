@@ -477,7 +477,9 @@ struct Decode {
     float* w;      // [nwaves][WC]   per-wavefront broadcast of w (and of the reference's w)
     float* up;     // [wrw][dv]      retrieval partials across row-wavefronts
     float* op;     // [wrw][dv]      readout partials across row-wavefronts
-    float* z;      // [kMaxCap] + [nwaves][kMaxCap]  bypass readout projections
+    float* z;      // [kMaxCap] + [nw][kMaxCap]  bypass readout projections
+    float* zk;     // [kMaxCap]  delta rule with a bypass: z_c = U_c^T k
+    float* bz;     // [dv]       delta rule with a bypass: b = W z
   };
 
   static __device__ __forceinline__ void decays(const StepArgs& a, const HeadEntry& he, int tile, int i0,
@@ -548,11 +550,15 @@ struct Decode {
     return p;
   }
 
+  // With a bypass (bz non-null) the retrieval adds the bypass's share b_j,
+  // u_j = fl(u~_j + b_j), and the row-wavefront 0 lanes holding column sums
+  // store the new bypass column W[:, n] = fp16(w) at wn.
   template <int BITS>
   static __device__ __forceinline__ void delta_w(const StepArgs& a, int tile, const float xs[8][8],
                                                  const float kf[8], const float mul[8], const float kap[8],
                                                  bool fast, const DwPre& pre, float wv[8], float* wl,
-                                                 float* up, int wrw, int wr, int j0, int lane, int wave) {
+                                                 float* up, int wrw, int wr, int j0, int lane, int wave,
+                                                 const float* bz = nullptr, __half* wn = nullptr) {
     float v8[8];
     if (fast) {
 #pragma unroll
@@ -589,8 +595,13 @@ struct Decode {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int c = xtree_col<NB>(s, lane);
-      const float w = kHad ? v8[s] : __fmul_rn(be, __fsub_rn(pre.v[s], __fmul_rn(al, v8[s])));
-      if (NB < 4 || ((lane >> 2) & 1) == 0) wrow[8 * lc + c] = w;
+      const float u = (kBypass && bz) ? __fadd_rn(v8[s], bz[j0 + c]) : v8[s];
+      const float w = kHad ? u : __fmul_rn(be, __fsub_rn(pre.v[s], __fmul_rn(al, u)));
+      const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
+      if (writer) wrow[8 * lc + c] = w;
+      if constexpr (kBypass) {
+        if (writer && wr == 0) wn[j0 + c] = __float2half_rn(w);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -647,7 +658,8 @@ struct Decode {
 
   template <int BITS, bool BOOST = false>
   static __device__ __forceinline__ void body(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                              const Lds& L, uint32_t& flags) {
+                                              const Lds& L, uint32_t& flags, const BypassRegs* br = nullptr,
+                                              bool byp_regs = false) {
     const bool bf16 = SP::bf16(a), sf16 = SP::sf16(a);
     const int smode = SP::smode(a);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -741,7 +753,14 @@ struct Decode {
     // update B_t: w = v (loaded at the start), or the delta rule; INT4+Had
     // steps in the rotated basis, so its update vector is w~ = H w
     if constexpr (kHad && MODEL != kGDN) fwht8(wv, gl, lane);
-    if constexpr (MODEL == kGDN) {
+    if constexpr (MODEL == kGDN && kBypass) {
+      // the bypass's share of the retrieval, b = W (U^T k), from the values
+      // loaded at kernel start (the loop form ran before this step)
+      if (byp_regs && a.n > 0) gdn_bypass_retrieval_regs(a, SP::bf16(a), *br, L.zk, L.bz);
+      __half* wn = reinterpret_cast<__half*>(tb + he.bypass_w) + (size_t)a.n * a.dv;
+      delta_w<BITS>(a, tile, x, kf, smul, kap, fast, dwp, wv, L.w, L.up, wrw, wr, j0, lane, wave,
+                    a.n > 0 ? L.bz : nullptr, wn);
+    } else if constexpr (MODEL == kGDN) {
       delta_w<BITS == 32 ? 8 : BITS>(a, tile, x, kf, smul, kap, fast && !kDense, dwp, wv, L.w, L.up, wrw, wr, j0,
                                      lane, wave);
     }
@@ -1274,6 +1293,8 @@ struct Decode {
     L.up = L.w + nw * WC;                     // [2][wrw][dv]
     L.op = L.up + 2 * wrw * a.dv;             // [wrw][dv]
     L.z = L.op + wrw * a.dv;                  // [kMaxCap] + [nw][kMaxCap]
+    L.zk = L.z + kMaxCap * (1 + nw);          // [kMaxCap]
+    L.bz = L.zk + kMaxCap;                    // [dv]
     uint32_t flags = 0;
 
     // bypass: its loads join the state's (values held in registers) when
@@ -1281,22 +1302,29 @@ struct Decode {
     BypassRegs br;
     bool byp_regs = false;
     if constexpr (kBypass) {
-      byp_regs = bypass_regs_fit(a);
-      if (byp_regs) bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br);
-      else bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
+      byp_regs = bypass_regs_fit(a, MODEL);
+      if (byp_regs) {
+        bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br);
+      } else {
+        // the delta rule reads the bypass before the decay below rewrites U
+        if constexpr (MODEL == kGDN) {
+          if (a.n > 0) gdn_bypass_retrieval_loop(a, he, tb, tile, L.zk, L.bz);
+        }
+        bypass_decode_phase(a, he, tb, tile, L.z, MODEL);
+      }
     }
 
     if constexpr (kF32) {
       body<32, BOOST>(a, he, tb, tile, L, flags);
     } else {
       switch (he.bits) {
-        case 4: body<4, BOOST>(a, he, tb, tile, L, flags); break;
-        case 6: body<6, BOOST>(a, he, tb, tile, L, flags); break;
-        default: body<8, BOOST>(a, he, tb, tile, L, flags); break;
+        case 4: body<4, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
+        case 6: body<6, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
+        default: body<8, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
       }
     }
     if constexpr (kBypass) {
-      if (byp_regs) bypass_store(a, he, tb, tile, SP::bf16(a), br, L.z);
+      if (byp_regs) bypass_store(a, he, tb, tile, MODEL, SP::bf16(a), br, L.z);
     }
     // the staying window pairs: after the state's step, whose loads then go
     // out first (the pairs never touch the leaving pair's slot, which the
@@ -1335,7 +1363,12 @@ struct Decode {
       const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
       if (pp < P) {
         float part = 0.f;
-        if (kBypass && byp_regs) part = bypass_wz_part(a, SP::bf16(a), br, L.z);
+        if (kBypass && byp_regs) {
+          // the delta rule's new column is fp16(w_j), w as published by the
+          // first row-wavefront of column j's stripe
+          const float w_new = MODEL == kGDN ? L.w[(j / WC) * wrw * WC + j % WC] : 0.f;
+          part = bypass_wz_part(a, MODEL, SP::bf16(a), br, L.z, w_new);
+        }
         else
           for (int c = pp; c < cnt; c += P) part = __builtin_fmaf(wval(c, j), L.z[c], part);
         L.up[pp * a.dv + j] = part;

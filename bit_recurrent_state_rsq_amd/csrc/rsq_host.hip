@@ -143,8 +143,6 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   const bool yoked = c->scale_mode == RSQ_SCALE_YOKED && !p.all32;
   if (p.all32 && (p.bypass || c->bdr))
     return fail(RSQ_E_INVALID, "bits 32 (fp32 state) takes no bypass and no BDR");
-  if (p.bypass && c->model == RSQ_GDN)
-    return fail(RSQ_E_UNSUPPORTED, "the low-rank bypass is not implemented for the delta rule");
   if (p.bypass && yoked) return fail(RSQ_E_UNSUPPORTED, "yoked scales with a bypass are not implemented");
   if (p.cap > rsq::kMaxCap) return fail(RSQ_E_UNSUPPORTED, "bypass capacity %d > %d", p.cap, rsq::kMaxCap);
   if (c->hadamard != 0 && c->hadamard != 1) return fail(RSQ_E_INVALID, "hadamard %d", c->hadamard);
@@ -174,8 +172,10 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   if (G.threads > 512) return fail(RSQ_E_UNSUPPORTED, "d_k*d_v = %d exceeds 32768", c->d_k * c->d_v);
   if (c->model == RSQ_GDN && (c->d_k & (c->d_k - 1)))
     return fail(RSQ_E_UNSUPPORTED, "the delta rule needs a power-of-two d_k, got %d", c->d_k);
-  // per-wave w broadcast, 2 x retrieval partials, readout partials, bypass projections
-  G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64)) *
+  // per-wave w broadcast, 2 x retrieval partials, readout partials, bypass
+  // projections; with a bypass also the delta rule's U^T k and W (U^T k)
+  G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64) +
+                   (p.bypass ? rsq::kMaxCap + c->d_v : 0)) *
           sizeof(float);
   // the merge reduces its products over as many basis columns per pass as
   // the LDS holds (fewer passes, fewer barriers); at least 8

@@ -146,8 +146,52 @@ __device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const Hea
     acc = wave_sum64(acc);
     if (lane == 0) lds_z[c] = acc;
   }
-  for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
-    W[(size_t)n * a.dv + j] = __float2half_rn(in_elem(a.in_bf16, a.v, (size_t)tile * a.dv + j));
+  // the delta rule's column is fp16(w), written by the step once w is known
+  if (model != kGDN)
+    for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
+      W[(size_t)n * a.dv + j] = __float2half_rn(in_elem(a.in_bf16, a.v, (size_t)tile * a.dv + j));
+  __syncthreads();
+}
+
+// Gated DeltaNet with a bypass: the retrieval reads S = s_hat + U W^T, so it
+// needs b = W (U^T k) with U and W as they were before this step:
+//   z_c = pairwise sum over rows (row order) of fl(U_ic k_i)   -> zk[c]
+//   b_j = fma chain over c = 0 .. n-1 of (W_jc, z_c), from 0   -> bz[j]
+// This is the general form, for tiles the register path below does not hold:
+// column c belongs to wavefront c mod nw, lane l takes rows l R .. l R + R - 1
+// (R = d_k / 64, or one row for d_k < 64; d_k is a power of two), sums them
+// pairwise and the lanes then meet 1, 2, 4, ..., 32 apart (wave_sum64), which
+// is the pairwise tree over all rows. Ends with a barrier.
+__device__ __forceinline__ void gdn_bypass_retrieval_loop(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
+                                                          int tile, float* zk, float* bz) {
+  const __half* U = reinterpret_cast<const __half*>(tb + he.bypass_u);
+  const __half* W = reinterpret_cast<const __half*>(tb + he.bypass_w);
+  const int n = a.n;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int R = a.dk >= 64 ? a.dk >> 6 : 1;   // 1 .. 16
+  for (int c = wave; c < n; c += nw) {
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = lane * R + r;
+      p[r] = (r < R && i < a.dk)
+                 ? __fmul_rn(__half2float(U[(size_t)c * a.dk + i]), in_elem(a.in_bf16, a.k, (size_t)tile * a.dk + i))
+                 : 0.f;
+    }
+    // pairwise over the lane's rows: the entries past R are zero subtrees
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2 * h) p[r] = __fadd_rn(p[r], p[r + h]);
+    const float z = wave_sum64(p[0]);
+    if (lane == 0) zk[c] = z;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
+    float b = 0.f;
+    for (int c = 0; c < n; ++c) b = __builtin_fmaf(__half2float(W[(size_t)c * a.dv + j]), zk[c], b);
+    bz[j] = b;
+  }
   __syncthreads();
 }
 
@@ -161,6 +205,9 @@ __device__ __forceinline__ void bypass_decode_phase(const StepArgs& a, const Hea
 // wavefront and, for the readout term, at most kBypWCols columns per
 // partial-sum thread group (P = blockDim / d_v groups).
 constexpr int kBypCols = 4, kBypWCols = 8;
+// the delta rule's register path holds every W column of its thread's row j
+// (the retrieval's b_j runs over all of them in order)
+constexpr int kBypWColsGdn = 16;
 struct BypassRegs {
   // raw loaded bits: nothing is converted until bypass_store, after the
   // state's own loads have been issued. Lane l holds rows 4l .. 4l + 3.
@@ -168,12 +215,15 @@ struct BypassRegs {
   float av[4];                 // a_i
   uint32_t kb[4];              // k_i (used by the wavefront that writes column n)
   uint32_t uv[kBypCols][2];    // U_ic of the wavefront's columns (binary16 pairs)
-  uint32_t wv[kBypWCols];      // W_jc of this thread's readout columns (binary16 bits)
-  uint32_t vb;                 // v_j (column n of W is fp16(v_j))
+  // W_jc of this thread's readout columns (binary16 bits); the delta rule
+  // holds columns 0 .. kBypWColsGdn - 1 of row j in every thread of the row
+  uint32_t wv[kBypWColsGdn];
+  uint32_t vb;                 // v_j (column n of W is fp16(v_j); not for the delta rule)
 };
 
-__device__ __forceinline__ bool bypass_regs_fit(const StepArgs& a) {
+__device__ __forceinline__ bool bypass_regs_fit(const StepArgs& a, int model) {
   const int nw = blockDim.x >> 6, P = (int)(blockDim.x / a.dv);
+  if (model == kGDN) return a.dk <= 256 && a.n + 1 <= kBypCols * nw && P >= 1 && a.n < kBypWColsGdn;
   return a.dk <= 256 && a.n + 1 <= kBypCols * nw && P >= 1 && a.n + 1 <= kBypWCols * P;
 }
 
@@ -233,18 +283,63 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
     br.uv[m][0] = t.x, br.uv[m][1] = t.y;
   }
   // readout term: thread (pp, j) takes columns pp, pp + P, ... (column n is
-  // fp16(v_j), written this step: taken from v, not read back)
+  // fp16(v_j), written this step: taken from v, not read back). The delta
+  // rule's thread holds all of row j's columns before n (its column n is
+  // fp16(w_j), known only after the retrieval).
   const int P = (int)(blockDim.x / a.dv);
   const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
+  if (model == kGDN) {
+#pragma unroll
+    for (int m = 0; m < kBypWColsGdn; ++m) br.wv[m] = W[(size_t)min(m, ulast) * a.dv + j];
+    br.vb = 0u;
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < kBypWCols; ++m) br.wv[m] = W[(size_t)min(pp + P * m, wlast) * a.dv + j];
   br.vb = in_bits(bf16, a.v, (size_t)tile * a.dv + j);
 }
 
+// The delta rule's bypass retrieval from the register path (same sums and
+// order as gdn_bypass_retrieval_loop): lane l holds rows 4l .. 4l + 3, so the
+// lane's rows pairwise and then wave_sum64 give the pairwise row tree. Runs
+// before the retrieval of the stored state; ends with a barrier.
+__device__ __forceinline__ void gdn_bypass_retrieval_regs(const StepArgs& a, bool bf16, const BypassRegs& br,
+                                                          float* zk, float* bz) {
+  const int n = a.n;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const bool rows_ok = 4 * lane < a.dk;
+#pragma unroll
+  for (int m = 0; m < kBypCols; ++m) {
+    const int c = wave + nw * m;
+    if (c >= n) break;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __half u = __ushort_as_half((uint16_t)(br.uv[m][r >> 1] >> (16 * (r & 1))));
+      p[r] = __fmul_rn(__half2float(u), in4_at(bf16, br.kb, r));
+    }
+    const float acc = __fadd_rn(__fadd_rn(p[0], p[1]), __fadd_rn(p[2], p[3]));
+    const float z = wave_sum64(rows_ok ? acc : 0.f);
+    if (lane == 0) zk[c] = z;
+  }
+  __syncthreads();
+  const int P = (int)(blockDim.x / a.dv);
+  const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
+  if (pp == 0) {
+    float b = 0.f;
+#pragma unroll
+    for (int m = 0; m < kBypWColsGdn; ++m)
+      if (m < n) b = __builtin_fmaf(__half2float(__ushort_as_half((uint16_t)br.wv[m])), zk[m], b);
+    bz[j] = b;
+  }
+  (void)P;
+  __syncthreads();
+}
+
 // Decay and store of U, the new columns of U and W, and z_c = sum_i U_ic q_i
 // in lds_z (the lane's four rows in order, then a wave reduction).
 __device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                             bool bf16, BypassRegs& br, float* lds_z) {
+                                             int model, bool bf16, BypassRegs& br, float* lds_z) {
   uint16_t* U = reinterpret_cast<uint16_t*>(tb + he.bypass_u);
   __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
   const int n = a.n;
@@ -280,15 +375,28 @@ __device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry&
   const int P = (int)(blockDim.x / a.dv);
   const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
   pin(br.vb);
-  if (pp == n % P) W[(size_t)n * a.dv + j] = __float2half_rn(bits_in(bf16, br.vb));   // column n of row j
+  // column n of row j (the delta rule's, fp16(w_j), is written by the step)
+  if (model != kGDN && pp == n % P) W[(size_t)n * a.dv + j] = __float2half_rn(bits_in(bf16, br.vb));
 }
 
-// Readout term of the register path: this thread's share of (W z)_j.
-__device__ __forceinline__ float bypass_wz_part(const StepArgs& a, bool bf16, BypassRegs& br, const float* lds_z) {
+// Readout term of the register path: this thread's share of (W z)_j. The
+// delta rule passes its new column's fp16(w_j) as w_new.
+__device__ __forceinline__ float bypass_wz_part(const StepArgs& a, int model, bool bf16, BypassRegs& br,
+                                                const float* lds_z, float w_new) {
   const int P = (int)(blockDim.x / a.dv);
   const int pp = threadIdx.x / a.dv;
   const int cnt = a.n + 1;
   float part = 0.f;
+  if (model == kGDN) {
+    // thread pp takes columns pp, pp + P, ... of its held row
+#pragma unroll
+    for (int m = 0; m < kBypWColsGdn; ++m) {
+      pin(br.wv[m]);
+      const __half wh = m == a.n ? __float2half_rn(w_new) : __ushort_as_half((uint16_t)br.wv[m]);
+      if (m < cnt && m % P == pp) part = __builtin_fmaf(__half2float(wh), lds_z[m], part);
+    }
+    return part;
+  }
 #pragma unroll
   for (int m = 0; m < kBypWCols; ++m) {
     const int c = pp + P * m;

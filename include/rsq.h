@@ -92,7 +92,12 @@ enum {
  *                  (0.5 + bdr_eps) * s (bdr_eps >= 0.5 corrects every reversal
  *                  whose corrected code is inside the code range)
  *  lrb_k, lrb_m    Low-Rank Bypass: k residual columns kept by a merge, a merge
- *                  every m steps (capacity k + m fp16 column pairs); m = 0 = off
+ *                  every m steps (capacity k + m fp16 column pairs); m = 0 = off.
+ *                  Every update goes into the bypass as one column pair
+ *                  (fp16(k), fp16(w)) and the codes only decay between merges.
+ *                  With GDN the delta rule reads the stored state plus the
+ *                  bypass: u = s_hat^T k + W (U^T k) ("Preserving Updates ...",
+ *                  Table 6 GDN row, Tables 7 and 8)
  *  lrb_eps         merge threshold eps_L: |L_ij| > eps_L * s moves into the state
  *  gamma           RetNet only: host array [heads] of decays; NULL otherwise
  *  in_dtype        RSQ_F32 | RSQ_BF16: element type of q, k, v
@@ -118,8 +123,8 @@ enum {
  * Supported shapes (others return RSQ_E_UNSUPPORTED): d_v a multiple of
  * 8 * max(4, group / 8); d_k a multiple of 512 / max(4, group / 8) rows per
  * wavefront (128 for group <= 32, 64 for group 64, 32 for group 128) with
- * d_k * d_v <= 32768; GDN needs d_k to be a power of two; the bypass runs
- * with RetNet, Mamba2 and GLA; yoked scales run without a bypass.
+ * d_k * d_v <= 32768; GDN needs d_k to be a power of two; yoked scales run
+ * without a bypass.
  */
 typedef struct rsq_config {
   uint32_t abi_version;

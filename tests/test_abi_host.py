@@ -52,7 +52,7 @@ GOOD = dict(model="gdn", batch=2, heads=4, d_k=128, d_v=128, group=32, bits=4,
     (dict(model="retnet"), _abi.RSQ_E_INVALID),                    # RetNet without gamma
     (dict(model="gla", gamma=[0.9] * 4), _abi.RSQ_E_INVALID),      # gamma for a non-RetNet model
     (dict(lrb_k=2, lrb_m=0), _abi.RSQ_E_INVALID),
-    (dict(lrb_k=1, lrb_m=15), _abi.RSQ_E_UNSUPPORTED),             # bypass with the delta rule
+    (dict(lrb_k=1, lrb_m=15, scale_mode="yoked"), _abi.RSQ_E_UNSUPPORTED),   # yoked scales with a bypass
     (dict(model="gla", lrb_k=20, lrb_m=20), _abi.RSQ_E_UNSUPPORTED),
     (dict(model="gla", lrb_k=1, lrb_m=3, scale_mode="yoked"), _abi.RSQ_E_UNSUPPORTED),
     (dict(d_k=96), _abi.RSQ_E_UNSUPPORTED),                        # not a multiple of 128 rows
@@ -68,6 +68,12 @@ def test_invalid_configurations_are_rejected(change, code):
     got, msg = _status_of(**kw)
     assert got == code, msg
     assert msg and msg != "no error"
+
+
+def test_delta_rule_with_a_bypass_is_accepted():
+    """Gated DeltaNet with the low-rank bypass at Table 6's setting (k = 1, m = 15)."""
+    got, msg = _status_of(**dict(GOOD, lrb_k=1, lrb_m=15, lrb_eps=0.5, bdr=True, bdr_eps=0.3))
+    assert got == _abi.RSQ_OK, msg
 
 
 def test_bad_abi_version():
