@@ -4,18 +4,31 @@
 
 A step is one decode step of every (batch, head) tile of the workload: load
 and dequantize the state, decay, update (the Gated DeltaNet delta rule for the
-default workload), read out o_t, rescale, requantize, store in place. Inputs
-for 64 distinct steps are generated once and cycled; they sit in HBM before
-the timed region starts. The state is rotated over enough independent state
-sets (>= 1 GiB) that the 256 MB Infinity Cache cannot hold them, so every
-step streams its state from HBM ("cold"; --warm times a single state set).
+default workload), read out o_t, rescale, requantize, store in place; with a
+low-rank bypass, a merge follows every m-th step and is part of the step's
+cost. The default workload is the large-batch Gated DeltaNet serving step
+(512 x 32 heads of 128 x 128, per-head INT8/INT6/INT4). Inputs for 64
+distinct steps are generated once and cycled; they sit in HBM before the
+timed region starts. The state is rotated over enough independent state sets
+(>= 1 GiB) that the 256 MB Infinity Cache cannot hold them, so every step
+streams its state from HBM ("cold"; --warm times a single state set). Each
+state set is first brought to decode step `--age` (untimed set-up), so the
+timed steps see a decoding state rather than a fresh zero one.
 
 Prints one JSON line (rank 0). `value` is state-updates per second
 (batch * heads * steps / wall time). `roofline.achieved` is the algorithmic
-bytes of one launch divided by the mean kernel duration from HIP events on the
-launch stream; `roofline.traffic` comes from committed rocprofv3 counter
-summaries when they were taken on the current kernel sources, else null.
-`cpu_baseline` times the CPU oracle (test infrastructure) on a bounded sample.
+bytes of one step (decode launch plus the amortized merges) divided by the
+mean device time of one step from HIP events on the launch stream;
+`roofline.frac` is against the 8 TB/s HBM peak and `frac_of_copy` against a
+plain device copy measured on the same GPU. `roofline.traffic` comes from
+committed rocprofv3 counter summaries when they were taken on the current
+kernel sources, else null. `fp32_state` times the same step on an fp32 state
+(bits = 32, no quantizer) of the same shape under the same protocol: the
+quantized step's speed-up over it. `quality` (default workload) runs a
+quantized state and an fp32 state from zero on the same device-drawn inputs
+for the whole horizon and reports the relative L2 error of o_t at a quarter,
+half and all of it, per bit width and overall. `cpu_baseline` times the CPU
+oracle (test infrastructure) on a bounded sample.
 """
 import argparse
 import ctypes
@@ -256,15 +269,180 @@ def accounting_report(torch, steps, batch=4, heads=4):
         }), flush=True)
 
 
+def _dev_inputs(torch, w, inp):
+    d = {}
+    for name in ("q", "k", "v"):
+        if w.in_dtype == "bf16":
+            d[name] = torch.from_numpy(np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)).cuda().view(torch.bfloat16)
+        else:
+            d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda()
+    for name in ("alpha", "beta"):
+        d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda() if name in inp else None
+    return d
+
+
+def time_steps(torch, rsq, w, kw, dev, K, warmup, age, warm, min_set_bytes, out):
+    """The timed protocol for one state configuration: rotate over state sets
+    of >= min_set_bytes (one set if warm), bring each to decode step `age`,
+    run `warmup` untimed steps, then time K steps. Decode launches are timed in
+    groups of up to GROUP consecutive steps by HIP events on their first and
+    last dispatch; each merge carries its own pair. Returns a dict."""
+    per_state = rsq.state_bytes(**kw)
+    nsets = 1 if warm else int(np.ceil(min_set_bytes / per_state))
+    states = [rsq.State(**kw) for _ in range(nsets)]
+    cap = w.lrb_k + w.lrb_m if w.lrb_m else 0
+    stream = torch.cuda.current_stream()
+    bound = {}
+
+    def step_fn(i, s):
+        key = (i, s % len(dev))
+        if key not in bound:
+            d = dev[key[1]]
+            bound[key] = states[i].bind_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"], out=out, stream=stream)
+        return bound[key]
+
+    def maybe_merge(i):
+        if cap and states[i].counters()[1] == cap:
+            states[i].merge_bypass(stream=stream)
+
+    for i in range(nsets):
+        for s in range(age):
+            step_fn(i, s)()
+            maybe_merge(i)
+    for s in range(warmup):
+        step_fn(s % nsets, age + s // nsets)()
+        maybe_merge(s % nsets)
+    torch.cuda.synchronize()
+
+    # which timed steps are followed by a merge (fills evolve deterministically)
+    merge_after = set()
+    fill = [st.counters()[1] for st in states]
+    if cap:
+        for s in range(K):
+            i = s % nsets
+            fill[i] += 1
+            if fill[i] == cap:
+                merge_after.add(s)
+                fill[i] = w.lrb_k
+    groups = []
+    g0 = 0
+    for s in range(K):
+        if s - g0 + 1 == GROUP or s in merge_after or s == K - 1:
+            groups.append((g0, s + 1))
+            g0 = s + 1
+    hip = _HipEvents(2 * len(groups) + 2 * len(merge_after))
+    base = [st.counters()[0] for st in states]
+    calls = [step_fn(s % nsets, base[s % nsets] + s // nsets) for s in range(K)]
+    ev_of = {}
+    for gi, (a0, a1) in enumerate(groups):
+        ev_of[a0] = [hip.ev[2 * gi], None]
+        ev_of.setdefault(a1 - 1, [None, None])[1] = hip.ev[2 * gi + 1]
+    mev = {s: (hip.ev[2 * len(groups) + 2 * mi], hip.ev[2 * len(groups) + 2 * mi + 1])
+           for mi, s in enumerate(sorted(merge_after))}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev_of.get(s)
+        if e is None:
+            calls[s]()
+        else:
+            calls[s](e[0], e[1])
+        if s in merge_after:
+            states[s % nsets].merge_bypass(stream=stream, start_event=mev[s][0], stop_event=mev[s][1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if cap and [st.counters()[1] for st in states] != fill:
+        raise RuntimeError("bypass fill differs from the merge schedule")
+    group_ms = np.array([hip.elapsed(2 * gi, 2 * gi + 1) for gi in range(len(groups))])
+    group_n = np.array([a1 - a0 for a0, a1 in groups])
+    merge_ms = np.array([hip.elapsed(2 * len(groups) + 2 * mi, 2 * len(groups) + 2 * mi + 1)
+                         for mi in range(len(merge_after))])
+    hip.destroy()
+    flags = [st.get_status() for st in states[: min(4, nsets)]]
+    extra_merges = 0
+    if cap and len(merge_ms) < 8:
+        # too few state sets filled inside the timed region: after it, fill up
+        # to 8 of them (untimed decode steps) and time their merges alone
+        nm = min(8, nsets)
+        ev = _HipEvents(2 * nm)
+        for i in range(nm):
+            while states[i].counters()[1] < cap:
+                step_fn(i, states[i].counters()[0])()
+        torch.cuda.synchronize()
+        for i in range(nm):
+            states[i].merge_bypass(stream=stream, start_event=ev.ev[2 * i], stop_event=ev.ev[2 * i + 1])
+        torch.cuda.synchronize()
+        merge_ms = np.concatenate([merge_ms, [ev.elapsed(2 * i, 2 * i + 1) for i in range(nm)]])
+        ev.destroy()
+        extra_merges = nm
+    decode_ms = float(group_ms.sum() / group_n.sum())
+    merge_mean = float(merge_ms.mean()) if len(merge_ms) else None
+    res = {"nsets": nsets, "per_state": per_state, "wall": wall, "decode_ms": decode_ms,
+           "decode_median_ms": float(np.median(group_ms / group_n)),
+           "merges": len(merge_after), "extra_merges": extra_merges, "merge_ms": merge_mean,
+           # device time of one step: a decode launch plus 1/m of a merge
+           "step_ms": decode_ms + (merge_mean / w.lrb_m if cap else 0.0), "flags": flags}
+    del states, bound, calls
+    return res
+
+
+def quality_report(torch, rsq, w, hb, steps):
+    """o_t of a quantized state against an fp32 state (bits = 32) of the same
+    shape fed the same device-drawn inputs from a zero state, for `steps`
+    steps: relative L2 error over [B, H, d_v] at a quarter, half and all of the
+    horizon, overall and per bit width."""
+    from rsq_workloads import static_params
+    from rsq_workloads.gen_device import device_step_inputs
+    kwq = rsq.config_kwargs_from(w, head_bits=hb if (w.mixed_bits or w.head_bits) else None)
+    w32 = w.with_(bits=32, mixed_bits=None, head_bits=None, lrb_k=0, lrb_m=0, bdr=False, scale_mode="dynamic",
+                  hadamard=False, pw_window=0)
+    kw32 = rsq.config_kwargs_from(w32)
+    sq, s32 = rsq.State(**kwq), rsq.State(**kw32)
+    cap = w.lrb_k + w.lrb_m if w.lrb_m else 0
+    a_log = static_params(w).get("a_log")
+    oq = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
+    o32 = torch.empty_like(oq)
+    marks = sorted({steps // 4, steps // 2, steps})
+    classes = {b: torch.as_tensor(np.flatnonzero(hb == b), device="cuda") for b in sorted(set(int(x) for x in hb))}
+    rep = {}
+    for t in range(1, steps + 1):
+        d = device_step_inputs(w, t, a_log=a_log)
+        args = (d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+        sq.decode_step(*args, out=oq)
+        s32.decode_step(*args, out=o32)
+        if cap and sq.counters()[1] == cap:
+            sq.merge_bypass()
+        if t in marks:
+            def rel(a, b):
+                return float(torch.linalg.vector_norm((a - b).double()) / torch.linalg.vector_norm(b.double()))
+            r = {"all": rel(oq, o32)}
+            if len(classes) > 1:
+                for b, idx in classes.items():
+                    r["int%d" % b] = rel(oq[:, idx], o32[:, idx])
+            rep[str(t)] = r
+    torch.cuda.synchronize()
+    flags = sq.get_status()
+    del sq, s32
+    return {"reference": "fp32 state (bits = 32) of the same shape, same inputs", "steps": steps,
+            "o_rel_l2": rep, "status_flags": flags,
+            "inputs": "drawn on the device (rsq_workloads.gen_device, the workload's distributions, fresh every step)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before timing (default: 24 per rotated state set, at least 64)")
-    ap.add_argument("--config", type=int, default=1)
+                    help="untimed steps before timing (default: 4 per rotated state set, at least 16)")
+    ap.add_argument("--age", type=int, default=32,
+                    help="untimed set-up: bring every state set to this decode step first")
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--warm", action="store_true", help="time one state set in place (cache-warm)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fp32", action="store_true", help="skip the fp32-state comparator")
+    ap.add_argument("--quality", type=int, default=None, metavar="T",
+                    help="steps of the quantized-vs-fp32 o_t report (default: the workload's horizon for "
+                         "the default workload, 0 = skip)")
     ap.add_argument("--min-set-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-only", action="store_true",
                     help="only time a plain 1 GiB device copy (the reference for HBM counters)")
@@ -272,6 +450,8 @@ def main():
                     help="store the state rotated per group (the INT4+Had baseline)")
     ap.add_argument("--pw", type=int, default=0, metavar="W",
                     help="Gated DeltaNet: keep a pure-write window of W FP8 pairs beside the history")
+    ap.add_argument("--lrb", type=str, default=None, metavar="K,M",
+                    help="add a low-rank bypass of rank K merged every M steps (with BDR, eps_L 0.5, eps_B 0.3)")
     ap.add_argument("--accounting", type=int, default=0, metavar="T",
                     help="instead of timing, run the error accounting for T steps per Table 1 row")
     args = ap.parse_args()
@@ -298,119 +478,44 @@ def main():
         w = w.with_(hadamard=True)
     if args.pw:
         w = w.with_(pw_window=args.pw)
+    if args.lrb:
+        k, m = (int(x) for x in args.lrb.split(","))
+        w = w.with_(lrb_k=k, lrb_m=m, lrb_eps=0.5, bdr=True, bdr_eps=0.3)
     # the CPU baseline forks worker processes: do it before this process touches the GPU
     cpu = None if args.no_cpu else cpu_baseline(w)
     torch.cuda.set_device(0)
     copy_ref = copy_reference(torch)
     hb = head_bits_for(w)
-    kw = rsq.config_kwargs_from(w, head_bits=hb if w.mixed_bits else None)
-    per_state = rsq.state_bytes(**kw)
-    nsets = 1 if args.warm else int(np.ceil(args.min_set_bytes / per_state))
-    states = [rsq.State(**kw) for _ in range(nsets)]
+    kw = rsq.config_kwargs_from(w, head_bits=hb if (w.mixed_bits or w.head_bits) else None)
 
     pool = InputPool.build(w, 64)
-    dev = []
-    for inp in pool.steps:
-        d = {}
-        for name in ("q", "k", "v"):
-            if w.in_dtype == "bf16":
-                d[name] = torch.from_numpy(np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)).cuda().view(torch.bfloat16)
-            else:
-                d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda()
-        for name in ("alpha", "beta"):
-            d[name] = torch.from_numpy(np.ascontiguousarray(inp[name], np.float32)).cuda() if name in inp else None
-        dev.append(d)
+    dev = [_dev_inputs(torch, w, inp) for inp in pool.steps]
     out = torch.empty((w.batch, w.heads, w.d_v), dtype=torch.float32, device="cuda")
-    cap = w.lrb_k + w.lrb_m if w.lrb_m else 0
-
-    stream = torch.cuda.current_stream()
-    # one bound launch per (state set, input step) pair used by the loops below
-    bound = {}
-
-    def step_fn(s):
-        key = (s % nsets, s % len(dev))
-        if key not in bound:
-            d = dev[key[1]]
-            bound[key] = states[key[0]].bind_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"],
-                                                  out=out, stream=stream)
-        return bound[key]
-
-    def after(s):
-        st = states[s % nsets]
-        if cap and st.counters()[1] == cap:
-            st.merge_bypass(stream=stream)
-
-    if args.warmup is None:
-        args.warmup = max(64, 24 * nsets)
-    for s in range(args.warmup):
-        step_fn(s)()
-        after(s)
-    torch.cuda.synchronize()
-
     K = args.steps
-    # which timed steps are followed by a bypass merge (a state merges once its
-    # fill reaches k + m): the fill of every state evolves deterministically
-    merge_after = set()
-    if cap:
-        fill = [st.counters()[1] for st in states]
-        for s in range(K):
-            i = s % nsets
-            fill[i] += 1
-            if fill[i] == cap:
-                merge_after.add(s)
-                fill[i] = w.lrb_k
-    # decode-kernel durations: a start event rides on the first dispatch and a
-    # stop event on the last dispatch of each group of up to GROUP consecutive
-    # steps (events on every dispatch would stall the queue between launches);
-    # a group ends at a merge, so group times hold decode launches only
-    groups = []
-    g0 = 0
-    for s in range(K):
-        if s - g0 + 1 == GROUP or s in merge_after or s == K - 1:
-            groups.append((g0, s + 1))
-            g0 = s + 1
-    hip = _HipEvents(2 * len(groups))
-    calls = [step_fn(s) for s in range(K)]
-    ev_of = {}
-    for gi, (a0, a1) in enumerate(groups):
-        ev_of[a0] = [hip.ev[2 * gi], None]
-        ev_of.setdefault(a1 - 1, [None, None])[1] = hip.ev[2 * gi + 1]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        e = ev_of.get(s)
-        if e is None:
-            calls[s]()
-        else:
-            calls[s](e[0], e[1])
-        if s in merge_after:
-            states[s % nsets].merge_bypass(stream=stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if cap and [st.counters()[1] for st in states] != fill:
-        raise RuntimeError("bypass fill differs from the merge schedule")
-    group_ms = np.array([hip.elapsed(2 * gi, 2 * gi + 1) for gi in range(len(groups))])
-    group_n = np.array([a1 - a0 for a0, a1 in groups])
-    hip.destroy()
+    nsets_guess = 1 if args.warm else int(np.ceil(args.min_set_bytes / rsq.state_bytes(**kw)))
+    if args.warmup is None:
+        args.warmup = max(16, 4 * nsets_guess)
+    q = time_steps(torch, rsq, w, kw, dev, K, args.warmup, args.age, args.warm, args.min_set_bytes, out)
 
     bytes_step = rsq.workload_step_bytes(w.model, w.batch, hb, w.group, w.scale_dtype, w.d_k, w.d_v,
                                          w.in_dtype, w.lrb_k, w.lrb_m, w.pw_window)
+    merge_bytes = rsq.workload_merge_bytes(w.batch, hb, w.group, w.scale_dtype, w.d_k, w.d_v, w.lrb_k,
+                                           w.lrb_m) if w.lrb_m else 0
+    # one step's algorithmic bytes: the decode launch plus 1/m of a merge
+    bytes_e2e = bytes_step + (merge_bytes / w.lrb_m if w.lrb_m else 0)
     updates = w.batch * w.heads * K
-    value = updates / wall
-    mean_ms = float(group_ms.sum() / group_n.sum())
-    achieved = bytes_step / (mean_ms * 1e-3) / 1e9
-    traffic, tinfo = load_traffic(w.name + ("_had" if w.hadamard else "") + ("_pw%d" % w.pw_window if w.pw_window else ""),
-                                  bytes_step)
-    flags = [st.get_status() for st in states[: min(4, nsets)]]
+    achieved = bytes_e2e / (q["step_ms"] * 1e-3) / 1e9
+    traffic, tinfo = load_traffic(w.name + ("_had" if w.hadamard else "") + ("_pw%d" % w.pw_window if w.pw_window else "")
+                                  + ("_lrb%d_%d" % (w.lrb_k, w.lrb_m) if args.lrb else ""), bytes_step)
 
     res = {
         "metric": METRIC,
-        "value": value,
+        "value": updates / q["wall"],
         "unit": "state-updates/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": wall / K * 1e3,
+        "ms_per_step": q["wall"] / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -419,10 +524,13 @@ def main():
         "config": {
             "workload": w.name, "model": w.model, "batch": w.batch, "heads": w.heads,
             "d_k": w.d_k, "d_v": w.d_v,
-            "state": "int%s%s%s" % ("/".join(str(b) for b in sorted(set(hb))), "+had" if w.hadamard else "",
-                                    "+pw%d" % w.pw_window if w.pw_window else ""),
+            "state": "int%s%s%s%s" % ("/".join(str(b) for b in sorted(set(hb))), "+had" if w.hadamard else "",
+                                      "+pw%d" % w.pw_window if w.pw_window else "",
+                                      "+lrb%d/%d" % (w.lrb_k, w.lrb_m) if w.lrb_m else ""),
             "group": w.group, "scale": "%s %s" % (w.scale_mode, w.scale_dtype), "inputs": w.in_dtype,
-            "protocol": "warm (one state set)" if args.warm else "cold (%d state sets, %.2f GiB)" % (nsets, nsets * per_state / 2 ** 30),
+            "protocol": "warm (one state set)" if args.warm else
+                        "cold (%d state sets, %.2f GiB)" % (q["nsets"], q["nsets"] * q["per_state"] / 2 ** 30),
+            "state_age": args.age,
             "parallelism": "single GPU",
         },
         "roofline": {
@@ -432,18 +540,40 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            "frac_of_copy": achieved / copy_ref["gbs"],
         },
-        "kernel": {"name": "rsq::decode_kernel", "mean_us": mean_ms * 1e3,
-                   "median_us": float(np.median(group_ms / group_n)) * 1e3,
+        "kernel": {"name": "rsq::decode_kernel", "mean_us": q["decode_ms"] * 1e3,
+                   "median_us": q["decode_median_ms"] * 1e3,
                    "timing": "HIP events on the dispatches of the first and last launch of each "
                              "group of up to %d consecutive decode steps in the timed region "
-                             "(groups end at bypass merges)" % GROUP,
-                   "merges_in_timed_region": len(merge_after),
+                             "(groups end at bypass merges; each merge has its own pair)" % GROUP,
                    "algorithmic_bytes_per_launch": bytes_step,
-                   "hbm_gbs_wall": bytes_step * K / wall / 1e9},
-        "status_flags": flags,
+                   "decode_only_gbs": bytes_step / (q["decode_ms"] * 1e-3) / 1e9,
+                   "hbm_gbs_wall": bytes_e2e * K / q["wall"] / 1e9},
+        "status_flags": q["flags"],
         "copy_reference": copy_ref,
     }
+    if w.lrb_m:
+        res["merge"] = {"name": "rsq::merge_kernel", "merges_in_timed_region": q["merges"],
+                        "merges_timed_after": q["extra_merges"],
+                        "mean_us": q["merge_ms"] * 1e3 if q["merge_ms"] is not None else None,
+                        "algorithmic_bytes_per_merge": merge_bytes,
+                        "step_us_with_amortized_merge": q["step_ms"] * 1e3}
+    if not args.no_fp32:
+        w32 = w.with_(bits=32, mixed_bits=None, head_bits=None, lrb_k=0, lrb_m=0, bdr=False,
+                      scale_mode="dynamic", hadamard=False, pw_window=0)
+        kw32 = rsq.config_kwargs_from(w32)
+        f = time_steps(torch, rsq, w32, kw32, dev, K, args.warmup, args.age, args.warm, args.min_set_bytes, out)
+        b32 = rsq.workload_step_bytes(w.model, w.batch, [32] * w.heads, w.group, w.scale_dtype, w.d_k, w.d_v,
+                                      w.in_dtype)
+        res["fp32_state"] = {"step_us": f["step_ms"] * 1e3, "algorithmic_bytes_per_launch": b32,
+                             "gbs": b32 / (f["step_ms"] * 1e-3) / 1e9,
+                             "protocol": "cold (%d state sets, %.2f GiB)" % (f["nsets"], f["nsets"] * f["per_state"] / 2 ** 30),
+                             "speedup_of_quantized": f["step_ms"] / q["step_ms"],
+                             "state_bytes_ratio": f["per_state"] / q["per_state"]}
+    qsteps = args.quality if args.quality is not None else (w.steps if args.config == 4 else 0)
+    if qsteps:
+        res["quality"] = quality_report(torch, rsq, w, hb, qsteps)
     if cpu is not None:
         res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)

@@ -22,10 +22,10 @@ import numpy as np
 from . import _abi
 from ._abi import Error, check, lib
 from . import codec
-from .accounting import step_bytes_per_tile, workload_step_bytes
+from .accounting import step_bytes_per_tile, workload_step_bytes, workload_merge_bytes
 
 __all__ = ["State", "Error", "state_bytes", "make_config", "step_bytes_per_tile",
-           "workload_step_bytes", "allocate_head_bits", "ErrorAccounting"]
+           "workload_step_bytes", "workload_merge_bytes", "allocate_head_bits", "ErrorAccounting"]
 
 
 def make_config(model, batch, heads, d_k, d_v, group, bits=4, head_bits=None,
@@ -250,8 +250,13 @@ class State:
                 check(code)
         return issue
 
-    def merge_bypass(self, stream=None):
-        check(lib.rsq_merge_bypass(self.h, _stream_ptr(stream)))
+    def merge_bypass(self, stream=None, start_event=None, stop_event=None):
+        """rsq_merge_bypass; with events, rsq_merge_bypass_timed (recorded by
+        the merge kernel's own dispatch)."""
+        if start_event is None and stop_event is None:
+            check(lib.rsq_merge_bypass(self.h, _stream_ptr(stream)))
+        else:
+            check(lib.rsq_merge_bypass_timed(self.h, _stream_ptr(stream), start_event, stop_event))
 
     def readout(self, q, out=None, stream=None):
         torch = _torch()

@@ -32,7 +32,7 @@ F_NONFINITE, F_SCALE_OVERFLOW, F_CLIPPED = 1, 2, 4
 
 EXPORTS = ["rsq_state_bytes", "rsq_state_alloc", "rsq_state_free", "rsq_state_layout",
            "rsq_tile_sections", "rsq_state_counters", "rsq_decode_step", "rsq_decode_step_timed",
-           "rsq_decode_step_diag", "rsq_merge_bypass",
+           "rsq_decode_step_diag", "rsq_merge_bypass", "rsq_merge_bypass_timed",
            "rsq_readout", "rsq_get_status", "rsq_last_error", "rsq_abi_version", "rsq_allocate_head_bits"]
 
 
@@ -91,6 +91,7 @@ def _load():
         "rsq_decode_step_timed": (I32, [P, P, P, P, P, P, P, P, P, P]),
         "rsq_decode_step_diag": (I32, [P, P, P, P, P, P, P, P, P, P, P]),
         "rsq_merge_bypass": (I32, [P, P]),
+        "rsq_merge_bypass_timed": (I32, [P, P, P, P]),
         "rsq_readout": (I32, [P, P, P, P]),
         "rsq_get_status": (I32, [P, ctypes.POINTER(ctypes.c_uint32), P]),
         "rsq_last_error": (ctypes.c_char_p, []),

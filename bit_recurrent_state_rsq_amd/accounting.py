@@ -9,6 +9,9 @@ their values read, the leaving pair read and the new pair written, which is
 2 W d_k + (W + 1) d_v bytes. This is the figure
 the roofline fraction is computed from; hardware counters report the traffic
 actually moved.
+
+A bypass merge (every m steps) reads and writes the codes and step sizes,
+reads the k + m held column pairs and writes the k kept ones.
 """
 
 
@@ -24,6 +27,18 @@ def step_bytes_per_tile(bits, group, scale_bytes, d_k, d_v, in_bytes, gate_bytes
     if pw > 0:
         b += 2 * pw * d_k + (pw + 1) * d_v
     return b
+
+
+def merge_bytes_per_tile(bits, group, scale_bytes, d_k, d_v, k, m):
+    """Algorithmic bytes of one bypass merge of one tile."""
+    state = d_k * d_v * bits // 8 + d_k * (d_v // group) * scale_bytes
+    return 2 * state + (k + m) * 2 * (d_k + d_v) + k * 2 * (d_k + d_v)
+
+
+def workload_merge_bytes(batch, head_bits, group, scale_dtype, d_k, d_v, k, m):
+    """Total algorithmic bytes of one merge over batch x heads tiles."""
+    sb = 2 if scale_dtype == "f16" else 4
+    return batch * sum(merge_bytes_per_tile(int(b), group, sb, d_k, d_v, k, m) for b in head_bits)
 
 
 def gate_bytes(model, d_k):

@@ -578,17 +578,21 @@ rsq_status rsq_decode_step_diag(rsq_state* st, const void* q, const void* k, con
   return decode_step(st, q, k, v, alpha, beta, o, stream, nullptr, nullptr, &dg);
 }
 
-rsq_status rsq_merge_bypass(rsq_state* st, void* stream) {
+rsq_status rsq_merge_bypass_timed(rsq_state* st, void* stream, void* start_event, void* stop_event) {
   if (!st) return fail(RSQ_E_INVALID, "state is NULL");
   if (!st->bypass) return fail(RSQ_E_NO_BYPASS, "this state has no low-rank bypass");
   StepArgs a = base_args(st);
   a.t_next = st->t;
   rsq::DecodeFn fn = rsq::merge_kernel_for(st->geo.cl);
   if (!fn) return fail(RSQ_E_UNSUPPORTED, "no merge kernel for this configuration");
-  const rsq_status s = launch(fn, st, a, stream, nullptr, nullptr, st->geo.lds_merge);
+  const rsq_status s = launch(fn, st, a, stream, start_event, stop_event, st->geo.lds_merge);
   if (s != RSQ_OK) return s;
   st->n = st->cfg.lrb_k;
   return RSQ_OK;
+}
+
+rsq_status rsq_merge_bypass(rsq_state* st, void* stream) {
+  return rsq_merge_bypass_timed(st, stream, nullptr, nullptr);
 }
 
 rsq_status rsq_readout(const rsq_state* st, const void* q, float* o, void* stream) {

@@ -280,6 +280,11 @@ rsq_status rsq_decode_step_diag(rsq_state* st, const void* q, const void* k, con
  */
 rsq_status rsq_merge_bypass(rsq_state* st, void* stream);
 
+/* rsq_merge_bypass for profiling: the merge kernel's dispatch records
+ * start_event / stop_event (hipEvent_t, either may be NULL), as in
+ * rsq_decode_step_timed. */
+rsq_status rsq_merge_bypass_timed(rsq_state* st, void* stream, void* start_event, void* stop_event);
+
 /* o = deq(S)^T q (+ W (U^T q)); reads the state only. q as in decode_step. */
 rsq_status rsq_readout(const rsq_state* st, const void* q, float* o, void* stream);
 
