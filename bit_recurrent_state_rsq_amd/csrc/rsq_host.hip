@@ -317,6 +317,19 @@ bool one_round(rsq::DecodeFn fn, unsigned blocks, unsigned threads, size_t lds) 
   return (long)blocks <= it->second;
 }
 
+// The step count t and the bypass fill n (or the window's pair count) live in
+// the host handle and reach the kernels as launch arguments, so a graph
+// captured from such a step would replay the same column and slot every
+// time. Steps that read them are refused while the stream is capturing.
+rsq_status refuse_capture(void* stream, const char* what) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing((hipStream_t)stream, &cap);
+  if (e != hipSuccess) return hip_fail(e, "stream capture query");
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(RSQ_E_UNSUPPORTED, "%s cannot be captured in a graph: its launch arguments change every call", what);
+  return RSQ_OK;
+}
+
 rsq_status launch(rsq::DecodeFn fn, const rsq_state* st, const StepArgs& a, void* stream,
                   void* ev_start = nullptr, void* ev_stop = nullptr, size_t lds = 0) {
   const dim3 grid(st->cfg.batch * st->cfg.heads), block(st->geo.threads);
@@ -516,6 +529,10 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
     if (ptr && reinterpret_cast<uintptr_t>(ptr) % 16) return fail(RSQ_E_INVALID, "inputs must be 16-byte aligned");
   if (st->bypass && st->n >= st->cap)
     return fail(RSQ_E_BYPASS_FULL, "bypass holds %d of %d columns: call rsq_merge_bypass", st->n, st->cap);
+  if (st->bypass || st->pw) {
+    const rsq_status cs = refuse_capture(stream, "a decode step of a state with a bypass or a pure-write window");
+    if (cs != RSQ_OK) return cs;
+  }
   StepArgs a = base_args(st);
   a.q = q;
   a.k = k;
@@ -581,6 +598,10 @@ rsq_status rsq_decode_step_diag(rsq_state* st, const void* q, const void* k, con
 rsq_status rsq_merge_bypass_timed(rsq_state* st, void* stream, void* start_event, void* stop_event) {
   if (!st) return fail(RSQ_E_INVALID, "state is NULL");
   if (!st->bypass) return fail(RSQ_E_NO_BYPASS, "this state has no low-rank bypass");
+  {
+    const rsq_status cs = refuse_capture(stream, "a bypass merge");
+    if (cs != RSQ_OK) return cs;
+  }
   StepArgs a = base_args(st);
   a.t_next = st->t;
   rsq::DecodeFn fn = rsq::merge_kernel_for(st->geo.cl);

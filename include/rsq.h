@@ -229,6 +229,10 @@ rsq_status rsq_state_counters(const rsq_state* st, int64_t* t, int32_t* n);
  *         updated state before requantization (plus W (U^T q) with a bypass)
  * Inputs must be contiguous and 16-byte aligned. With a bypass, returns
  * RSQ_E_BYPASS_FULL once k+m columns are in use (call rsq_merge_bypass).
+ * Steps of states without a bypass or window can be captured in a HIP graph
+ * and replayed; with a bypass or a pure-write window the step's column or
+ * slot comes from the host handle, so such a step (and rsq_merge_bypass)
+ * returns RSQ_E_UNSUPPORTED while `stream` is capturing.
  */
 rsq_status rsq_decode_step(rsq_state* st, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, float* o, void* stream);

@@ -430,3 +430,24 @@ def test_fp32_state_free_run_matches_closed_form(model):
                 tol = 1e-4 if t < 48 else 1e-3
                 assert rel_l2(S32[tile], S) <= tol, (t, tile, rel_l2(S32[tile], S))
                 assert rel_l2(o[tile], cf.readout(S, inp["q"][b, h])) <= tol
+
+
+def test_bypass_steps_refuse_graph_capture():
+    """A bypass state's step takes its column from the host handle, so
+    capturing it in a graph is refused (RSQ_E_UNSUPPORTED); outside a capture
+    the same call runs."""
+    import torch
+    import bit_recurrent_state_rsq_amd as rsq
+    w = CONFIGS[3].with_(batch=1, heads=2)
+    st = make_state(w)
+    d = to_device(step_inputs(w, 1, static_params(w)), w)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(rsq.Error) as e:
+        with torch.cuda.graph(g, stream=side):
+            st.decode_step(d["q"], d["k"], d["v"], d["alpha"], None, stream=side)
+    assert e.value.code == rsq._abi.RSQ_E_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert st.counters() == (0, 0)
+    gpu_step(st, d)
+    assert st.counters() == (1, 1)
