@@ -18,13 +18,22 @@
 //                             largest-magnitude stored entry of every U column
 //                             positive (the first one on ties)
 //
-// The rank-k approximation is a subspace iteration started from the bypass's
-// own right factors W (the row space of L), a fixed number of rounds of
-//   Q <- orth(R Z);  Z <- R^T Q
-// with CholeskyQR2 as orth, then Rayleigh-Ritz: the p x p matrix Z^T Z is
-// diagonalised by cyclic Jacobi and its top k eigenpairs give the factors.
-// R stays in registers in the decode kernel's 8x8-chunk lane layout; the
-// bases, partial sums and the small matrices live in LDS.
+// The rank-k approximation works on the Gram matrix of R's narrower side:
+// C = R^T R (d_v x d_v) when d_v <= d_k, else C = R R^T. C is formed once on
+// the matrix cores: R is scaled by a power of two into binary16 range and
+// split into a high and a low binary16 part, and the three products hi*hi,
+// hi*lo and lo*hi accumulate in float32 (the dropped lo*lo term is below
+// 2^-22 of each product). A fixed number of subspace iterations
+//   Q <- orth(C Q)
+// start from the bypass's own factors on that side (which span the row or
+// column space of L), with C Q again on split binary16 matrix cores. orth is
+// CholeskyQR (CholeskyQR2 for the last basis), which every wavefront computes
+// for itself so that no barrier separates the Gram matrix, its Cholesky
+// factor and the triangular solve. Rayleigh-Ritz then diagonalises the p x p
+// matrix Q^T C Q by cyclic Jacobi; its top k eigenpairs (sigma^2, v) give the
+// narrow-side singular vectors Q v, and the other side's R (Q v) / sigma
+// comes from R, which every lane still holds in registers in the decode
+// kernel's 8x8-chunk layout.
 #include <algorithm>
 
 #include "rsq_kernels.hpp"
@@ -37,45 +46,102 @@ namespace rsq {
 // rank) needs more of them. With the warm start these bring the Frobenius
 // error within 1e-4 of the Eckart-Young optimum on the workloads' residuals.
 constexpr int kMergeItersWide = 5;    // p >= 4k + 4
+constexpr int kMergeItersMid = 6;     // p >= 3k + 4
 constexpr int kMergeItersNarrow = 12;
 constexpr int kJacobiSweeps = 12;  // upper bound; stops once the off-diagonal part is negligible
-constexpr int kChunkMin = 8, kChunkMax = 32;   // basis columns per cross-wavefront reduction pass
 constexpr int kSm = kMaxCap + 1;   // row stride of the small p x p matrices
+constexpr int kWs = kMaxCap + 4;   // row stride of the Gram / Cholesky scratch (16-byte rows)
+constexpr int kWsFloats = (2 * kMaxCap + 1) * kWs;   // L's rows, a row of 1/diagonal, L^-1's rows
+constexpr int kQScale = 12;        // an orthonormal basis times 2^12 fits binary16 with room for its low part
 // misc block layout (floats)
-constexpr int kMiscDinv = 0, kMiscOrder = kMaxCap, kMiscSroot = 2 * kMaxCap, kMiscFlag = 3 * kMaxCap,
-              kMiscSign = 4 * kMaxCap, kMiscRot = 5 * kMaxCap, kMiscFloats = 7 * kMaxCap;
+constexpr int kMiscOrder = 0, kMiscSroot = kMaxCap, kMiscSign = 2 * kMaxCap, kMiscFlag = 3 * kMaxCap,
+              kMiscWave = 3 * kMaxCap + 4,   // [8] maxima, [8] non-finite flags per wavefront
+              kMiscJac = 3 * kMaxCap + 20,   // [2][8][2] Jacobi off-diagonal / diagonal partial sums
+              kMiscSinv = 3 * kMaxCap + 52,  // [kMaxCap] sigma^-1/2
+              kMiscOrth = 4 * kMaxCap + 52,  // condition estimate and scale exponent of the last orth pass
+              kMiscFloats = 7 * kMaxCap;
 
-// LDS carve-up of the merge kernel (floats); the host sizes the launch with
-// merge_lds_floats().
-struct MergeLds {
-  float* zt;    // [cap][zs]       right basis, column c at zt + c * zs
-  float* yt;    // [cap][ys]       left basis
-  float* part;  // [stripes][chunk][rows]  per-wavefront-stripe partial sums
-  float* g;     // [kMaxCap][kSm]  Gram matrix / Cholesky factor
-  float* h0;    // [kMaxCap][kSm]  Jacobi: H, double buffered
-  float* h1;
-  float* v0;    // [kMaxCap][kSm]  Jacobi: eigenvectors, double buffered
-  float* v1;
-  float* misc;  // [kMiscFloats]   1/diag of the Cholesky factor, eigen order, sigma^1/2,
-                //                 the Jacobi stop flag, column signs
-};
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 
 __host__ __device__ inline int merge_zs(int dv) { return dv + 4; }
 __host__ __device__ inline int merge_ys(int dk) { return dk + 4; }
 
-constexpr int kTri = kMaxCap * (kMaxCap + 1) / 2;   // entries of a symmetric kMaxCap x kMaxCap matrix
-
-// floats of the partial-sum area: product stripes, or per-wavefront Gram partials
+// floats of the partial-sum area of the closing products with R
 __host__ __device__ inline size_t merge_part_floats(int dk, int dv, int wrw, int wcw, int chunk) {
-  const size_t prod = (size_t)chunk * (size_t)(wcw * dk > wrw * dv ? wcw * dk : wrw * dv);
-  const size_t gram = (size_t)wrw * wcw * kTri;
-  return prod > gram ? prod : gram;
+  return (size_t)chunk * (size_t)(wcw * dk > wrw * dv ? wcw * dk : wrw * dv);
+}
+
+// LDS carve-up of the merge kernel, in floats from the start of the dynamic
+// area (X and C in halves). One area is shared by phases that never overlap
+// in time; only `misc` lies outside it:
+//   staging       the bypass factors (binary16)
+//   phase B       X split: binary16 high and low planes, column-major, K + 8 halves per column
+//   phase C       q, y (bases, column-major, N + 4 floats per column), the split C
+//                 (row-major, N + 8 halves per row), the Gram / Cholesky scratch
+//   phase D       q (the final basis), the Jacobi buffers and rotations over C, then the closing
+//                 products' bases and partial sums
+struct MergeLayout {
+  int N, K, pc;       // narrow side, wide side, basis columns rounded up to 16
+  bool right;         // N = d_v: C = R^T R (else C = R R^T)
+  size_t xh, xl;      // split X (halves)
+  size_t ch, cl;      // split C (halves)
+  size_t q, y, ws;    // bases; the Gram / Cholesky scratch
+  size_t h0, h1, v0, v1, rot;   // Jacobi: H, V (double buffered), rotations [2][kMaxCap][4]
+  size_t zt, yt, part;   // closing products
+  size_t misc, total;
+};
+
+__host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int wcw, int cap, int chunk) {
+  MergeLayout L;
+  L.right = dv <= dk;
+  L.N = L.right ? dv : dk;
+  L.K = L.right ? dk : dv;
+  L.pc = (cap + 15) & ~15;
+  const int nw = wrw * wcw;
+  const size_t bs = (size_t)L.pc * (L.N + 4);
+  const size_t csz = (size_t)L.N * (L.N + 8);   // two binary16 planes = one float per element
+  const size_t stage = ((size_t)cap * (dk + dv) + 1) / 2;
+  const size_t xsz = (size_t)L.N * (L.K + 8);
+  L.xh = 0;
+  L.xl = (size_t)L.N * (L.K + 8);
+  L.q = 0;
+  L.y = bs;
+  L.ch = 2 * (2 * bs);
+  L.cl = L.ch + (size_t)L.N * (L.N + 8);
+  L.ws = 2 * bs + csz;
+  L.h0 = 2 * bs;
+  L.h1 = L.h0 + kMaxCap * kSm;
+  L.v0 = L.h1 + kMaxCap * kSm;
+  L.v1 = L.v0 + kMaxCap * kSm;
+  L.rot = L.v1 + kMaxCap * kSm;
+  L.zt = L.rot + 8 * kMaxCap;
+  L.yt = L.zt + (size_t)cap * merge_zs(dv);
+  L.part = L.yt + (size_t)cap * merge_ys(dk);
+  const size_t phase_c = L.ws + kWsFloats;
+  (void)nw;
+  const size_t phase_d = L.part + merge_part_floats(dk, dv, wrw, wcw, chunk);
+  size_t u = stage;
+  u = u > xsz ? u : xsz;
+  u = u > phase_c ? u : phase_c;
+  u = u > phase_d ? u : phase_d;
+  L.misc = (u + 3) & ~size_t(3);
+  L.total = L.misc + kMiscFloats;
+  return L;
 }
 
 size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int chunk) {
-  const size_t part = merge_part_floats(dk, dv, wrw, wcw, chunk);
-  return (size_t)cap * merge_zs(dv) + (size_t)cap * merge_ys(dk) + part + 5 * kMaxCap * kSm + kMiscFloats;
+  return merge_layout(dk, dv, wrw, wcw, cap, chunk).total;
 }
+
+// the closing products' view of the LDS (the register products with R)
+struct MergeLds {
+  float* zt;    // [cap][zs]       right vectors, column c at zt + c * zs
+  float* yt;    // [cap][ys]       left vectors
+  float* part;  // [stripes][chunk][rows]  per-wavefront-stripe partial sums
+};
 
 // sum over the CL column lanes of a wavefront (lane bits 0 .. log2(CL)-1);
 // every lane of the group ends with the same value (the adds commute)
@@ -112,18 +178,6 @@ __device__ __forceinline__ void load_half8(const __half* p, float out[8]) {
     out[2 * q] = __half2float(__ushort_as_half((uint16_t)(w[q] & 0xFFFFu)));
     out[2 * q + 1] = __half2float(__ushort_as_half((uint16_t)(w[q] >> 16)));
   }
-}
-
-// (a, b) with a <= b of the pi-th entry of the upper triangle of a p x p matrix, row by row
-__device__ __forceinline__ void tri_pair(int pi, int p, int& a, int& b) {
-  a = 0;
-  int rowlen = p;
-  while (pi >= rowlen) {
-    pi -= rowlen;
-    ++a;
-    --rowlen;
-  }
-  b = a + pi;
 }
 
 template <int CL>
@@ -357,130 +411,386 @@ struct Merge {
     }
   }
 
-  // ------------------------------------------------------------ small dense pieces
-  // gram[a][b] = sum_i X[a][i] X[b][i] (X column-major: column c at xt + c * xs).
-  // Wavefront w sums rows [w*m/nw, (w+1)*m/nw) for the pairs its lanes own;
-  // the per-wavefront partials are then added in wavefront order.
-  static __device__ __forceinline__ void gram(const Geo& g, const float* xt, int xs, int m, int p, float* gm,
-                                              float* part) {
-    const int npairs = p * (p + 1) / 2;
-    const int rows = (m + g.nw - 1) / g.nw;
-    const int r0 = g.wave * rows, r1 = min(m, r0 + rows);
-    for (int pi = g.lane; pi < npairs; pi += 64) {
-      int ca, cb;
-      tri_pair(pi, p, ca, cb);
-      const float* xa = xt + (size_t)ca * xs;
-      const float* xb = xt + (size_t)cb * xs;
-      float s0 = 0.f, s1 = 0.f;
-      int r = r0;
-      if ((rows & 3) == 0) {
-        // 16-byte reads: the row stride and the wavefront's first row are
-        // multiples of 4 floats
-        for (; r + 3 < r1; r += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(xa + r);
-          const float4 b4 = *reinterpret_cast<const float4*>(xb + r);
-          s0 = __builtin_fmaf(a4.x, b4.x, s0);
-          s1 = __builtin_fmaf(a4.y, b4.y, s1);
-          s0 = __builtin_fmaf(a4.z, b4.z, s0);
-          s1 = __builtin_fmaf(a4.w, b4.w, s1);
+  // ------------------------------------------------------------ the factorisation on the matrix cores
+  static __device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+  }
+
+  // e with m 2^e in [2^14, 2^15) for a finite m > 0 (binary16's largest finite is 65504)
+  static __device__ __forceinline__ int fit_exp(float m) {
+    int ex;
+    frexpf(m, &ex);
+    return 15 - ex;
+  }
+
+  // v 2^e as binary16 high and low parts: hi = RN16(x), lo = RN16(x - hi), the
+  // difference being exact in float32
+  static __device__ __forceinline__ void split8(const float v[8], int e, h8v& hi, h8v& lo) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float x = ldexpf(v[t], e);
+      const _Float16 h = (_Float16)x;
+      hi[t] = h;
+      lo[t] = (_Float16)__fsub_rn(x, (float)h);
+    }
+  }
+
+  // X from the lane's chunk of R, times 2^e and split. X is R (its columns are
+  // R's columns) when d_v <= d_k, else R^T; K is X's row index.
+  static __device__ __forceinline__ void write_x(const Geo& g, const MergeLayout& ML, const float R[8][8], int e,
+                                                 _Float16* xh, _Float16* xl) {
+    const size_t xs = (size_t)ML.K + 8;
+    if (ML.right) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = R[t][c];
+        h8v hi, lo;
+        split8(v, e, hi, lo);
+        *reinterpret_cast<h8v*>(xh + (size_t)(g.j0 + c) * xs + g.i0) = hi;
+        *reinterpret_cast<h8v*>(xl + (size_t)(g.j0 + c) * xs + g.i0) = lo;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        h8v hi, lo;
+        split8(R[r], e, hi, lo);
+        *reinterpret_cast<h8v*>(xh + (size_t)(g.i0 + r) * xs + g.j0) = hi;
+        *reinterpret_cast<h8v*>(xl + (size_t)(g.i0 + r) * xs + g.j0) = lo;
+      }
+    }
+  }
+
+  // C = X^T X (N x N) in 32 x 32 blocks, block b = J1 * (N/32) + J2 holding
+  // C[J1 block rows][J2 block columns]; wavefront w takes blocks w, w + nw, ...
+  // (at most four: N = 128 implies at least four wavefronts). Lane l of a block
+  // reads X's columns J*32 + l%32 at rows 16 s + 8 (l/32) .. + 8; the three
+  // products hi*hi, hi*lo, lo*hi accumulate in float32.
+  static __device__ __forceinline__ void form_c(const Geo& g, const MergeLayout& ML, const _Float16* xh,
+                                                const _Float16* xl, f16v acc[4]) {
+    const int nb = ML.N / 32, ksteps = ML.K / 16;
+    const size_t xs = (size_t)ML.K + 8;
+    const int l = g.lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = g.wave + u * g.nw;
+      f16v c = {};
+      if (b < nb * nb) {
+        const int J1 = b / nb, J2 = b - J1 * nb;
+        const size_t ka = (size_t)(J1 * 32 + (l & 31)) * xs + 8 * (l >> 5);
+        const size_t kb = (size_t)(J2 * 32 + (l & 31)) * xs + 8 * (l >> 5);
+        for (int s = 0; s < ksteps; ++s) {
+          const h8v a_h = *reinterpret_cast<const h8v*>(xh + ka + 16 * s);
+          const h8v a_l = *reinterpret_cast<const h8v*>(xl + ka + 16 * s);
+          const h8v b_h = *reinterpret_cast<const h8v*>(xh + kb + 16 * s);
+          const h8v b_l = *reinterpret_cast<const h8v*>(xl + kb + 16 * s);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b_h, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_h, b_l, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_l, b_h, c, 0, 0, 0);
         }
       }
-      for (; r + 1 < r1; r += 2) {
-        s0 = __builtin_fmaf(xa[r], xb[r], s0);
-        s1 = __builtin_fmaf(xa[r + 1], xb[r + 1], s1);
-      }
-      if (r < r1) s0 = __builtin_fmaf(xa[r], xb[r], s0);
-      part[g.wave * kTri + pi] = __fadd_rn(s0, s1);
-    }
-    __syncthreads();
-    for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
-      float s = part[pi];
-      for (int w = 1; w < g.nw; ++w) s = __fadd_rn(s, part[w * kTri + pi]);
-      int ca, cb;
-      tri_pair(pi, p, ca, cb);
-      gm[ca * kSm + cb] = s;
-      gm[cb * kSm + ca] = s;
-    }
-    __syncthreads();
-  }
-
-  // G = L L^T for the p x p Gram matrix in gm (row stride kSm), p <= P. Lane i
-  // holds row i; column k of L reaches the other lanes through readlane.
-  // Writes L (rows, stride kMaxCap; only the entries left of the diagonal
-  // matter) to lt and 1/L_kk to dinv (0 for a dropped column).
-  template <int P>
-  static __device__ __forceinline__ void cholesky(int i, int p, const float* gm, float* dinv, float* lt) {
-    float row[P];
-#pragma unroll
-    for (int c = 0; c < P; ++c) row[c] = (i < p && c < p) ? gm[i * kSm + c] : 0.f;
-    const float gii = (i < p) ? gm[i * kSm + i] : 0.f;
-#pragma unroll
-    for (int k = 0; k < P; ++k) {
-      const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row[k]), k));
-      const float gkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gii), k));
-      const bool live = piv > 1e-6f * gkk && piv > 0.f;
-      // 1/sqrt to about an ulp is plenty: the second pass of CholeskyQR2
-      // removes what the first leaves
-      const float di = live ? __builtin_amdgcn_rsqf(piv) : 0.f;
-      // lanes i > k get L_ik; the other lanes only touch the upper
-      // triangle, which is never read (the diagonal is kept as 1/d)
-      const float lik = __fmul_rn(row[k], di);
-      row[k] = lik;
-      if (i == 0) dinv[k] = di;
-#pragma unroll
-      for (int j = k + 1; j < P; ++j) {
-        const float ljk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lik), j));
-        row[j] = __fsub_rn(row[j], __fmul_rn(lik, ljk));
-      }
-    }
-    if (i < p) {
-#pragma unroll
-      for (int c = 0; c < P; c += 4)
-        *reinterpret_cast<float4*>(lt + i * kMaxCap + c) = make_float4(row[c], row[c + 1], row[c + 2], row[c + 3]);
+      acc[u] = c;
     }
   }
 
-  // In place: X <- X L^-T with G = X^T X = L L^T (Cholesky), `passes` times
-  // (2: CholeskyQR2). A column whose remaining norm is below 1e-3 of its own
-  // (pivot below 1e-6 of its Gram diagonal) gets 1/diag = 0: it drops out.
-  static __device__ __forceinline__ void orth(const Geo& g, float* xt, int xs, int m, int p, const MergeLds& S,
-                                              int passes) {
-    float* dinv = S.misc + kMiscDinv;
-    float* lt = S.h1;    // L, row stride kMaxCap (16-byte aligned rows); free outside the Jacobi
-    for (int pass = 0; pass < passes; ++pass) {
-      gram(g, xt, xs, m, p, S.g, S.part);
-      if (g.wave == 0) {
-        // p rounded up to a multiple of 4 or 8 fixes the loop bounds; the
-        // padded columns are zero and drop out like any dependent column
-        if (p <= 8) cholesky<8>(g.lane, p, S.g, dinv, lt);
-        else if (p <= 16) cholesky<16>(g.lane, p, S.g, dinv, lt);
-        else if (p <= 20) cholesky<20>(g.lane, p, S.g, dinv, lt);
-        else if (p <= 24) cholesky<24>(g.lane, p, S.g, dinv, lt);
-        else cholesky<32>(g.lane, p, S.g, dinv, lt);
+  // The blocks of form_c times 2^e, split, into C's area (row-major, N + 8
+  // halves per row). Register r of lane l holds C[J1*32 + 8(r/4) + 4(l/32) + r%4][J2*32 + l%32];
+  // C is symmetric, so each block is written to (J2, J1) with rows and columns
+  // exchanged, four consecutive columns per store.
+  static __device__ __forceinline__ void store_c(const Geo& g, const MergeLayout& ML, const f16v acc[4], int e,
+                                                 _Float16* chh, _Float16* cll) {
+    const int nb = ML.N / 32;
+    const size_t cs = (size_t)ML.N + 8;
+    const int l = g.lane;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int b = g.wave + u * g.nw;
+      if (b < nb * nb) {
+        const int J1 = b / nb, J2 = b - J1 * nb;
+        const size_t row = (size_t)(J2 * 32 + (l & 31)) * cs;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          h4v hi, lo;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float x = ldexpf(acc[u][4 * r4 + t], e);
+            const _Float16 h = (_Float16)x;
+            hi[t] = h;
+            lo[t] = (_Float16)__fsub_rn(x, (float)h);
+          }
+          const size_t col = (size_t)J1 * 32 + 8 * r4 + 4 * (l >> 5);
+          *reinterpret_cast<h4v*>(chh + row + col) = hi;
+          *reinterpret_cast<h4v*>(cll + row + col) = lo;
+        }
       }
-      __syncthreads();
-      // forward substitution per row of X, in registers
-      for (int r = threadIdx.x; r < m; r += blockDim.x) {
-        float v[kMaxCap];
+    }
+  }
+
+  // Y (N x pc) = C Q 2^qe in 16 x 16 output blocks over the wavefronts (each
+  // wavefront's largest output magnitude to wmax[wave]):
+  // C's split rows as the A operand, the basis times 2^qe split as B.
+  // Lane l of a block reads C row M0 + l%16 and basis column n0 + l%16 at
+  // 32 s + 8 (l/16) .. + 8 and gets Y[M0 + 4 (l/16) + r][n0 + l%16] back.
+  static __device__ __forceinline__ void cq(const Geo& g, const MergeLayout& ML, const _Float16* chh,
+                                            const _Float16* cll, const float* q, float* y, int qe, float* wmax) {
+    const int N = ML.N;
+    const int nbr = N / 16, nbc = ML.pc / 16;
+    const size_t cs = (size_t)N + 8, bs = (size_t)N + 4;
+    const int l = g.lane;
+    float m = 0.f;
+    for (int b = g.wave; b < nbr * nbc; b += g.nw) {
+      const int M0 = (b % nbr) * 16, n0 = (b / nbr) * 16;
+      const size_t ar = (size_t)(M0 + (l & 15)) * cs + 8 * (l >> 4);
+      const float* qc = q + (size_t)(n0 + (l & 15)) * bs + 8 * (l >> 4);
+      f4v acc = {};
+      for (int s = 0; s < N / 32; ++s) {
+        const h8v a_h = *reinterpret_cast<const h8v*>(chh + ar + 32 * s);
+        const h8v a_l = *reinterpret_cast<const h8v*>(cll + ar + 32 * s);
+        float v[8];
+        loadf8(qc + 32 * s, v);
+        h8v b_h, b_l;
+        split8(v, qe, b_h, b_l);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h, b_h, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_h, b_l, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_l, b_h, acc, 0, 0, 0);
+      }
+      *reinterpret_cast<f4v*>(y + (size_t)(n0 + (l & 15)) * bs + M0 + 4 * (l >> 4)) = acc;
 #pragma unroll
-        for (int c = 0; c < kMaxCap; ++c) {
-          if (c < p) {
-            float acc = xt[(size_t)c * xs + r];
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[r]));
+    }
+    m = wave_max(m);
+    if (l == 0) wmax[g.wave] = m;
+  }
+
+  // Largest magnitude over the lane's fragments of a basis (columns < p) and
+  // its wavefront maximum
+  template <int NC>
+  static __device__ __forceinline__ float basis_max(const Geo& g, const float* src, int N, int p) {
+    const size_t bs = (size_t)N + 4;
+    float m = 0.f;
 #pragma unroll
-            for (int j0 = 0; j0 < c; j0 += 4) {
-              const float4 l4 = *reinterpret_cast<const float4*>(lt + c * kMaxCap + j0);
-              acc = __fsub_rn(acc, __fmul_rn(l4.x, v[j0]));
-              if (j0 + 1 < c) acc = __fsub_rn(acc, __fmul_rn(l4.y, v[j0 + 1]));
-              if (j0 + 2 < c) acc = __fsub_rn(acc, __fmul_rn(l4.z, v[j0 + 2]));
-              if (j0 + 3 < c) acc = __fsub_rn(acc, __fmul_rn(l4.w, v[j0 + 3]));
-            }
-            v[c] = __fmul_rn(acc, dinv[c]);
-            xt[(size_t)c * xs + r] = v[c];
+    for (int cb = 0; cb < NC; ++cb) {
+      const int col = cb * 16 + (g.lane & 15);
+      for (int s = 0; s < N / 32; ++s) {
+        if (col < p) {
+          float v[8];
+          loadf8(src + (size_t)col * bs + 32 * s + 8 * (g.lane >> 4), v);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) m = fmaxf(m, fabsf(v[t]));
+        }
+      }
+    }
+    return wave_max(m);
+  }
+
+  // the lane's A/B fragment of basis column cb*16 + l%16 (zero past p), rows 32 s + 8 (l/16) .. + 8, split
+  static __device__ __forceinline__ void basis_frag(const Geo& g, const float* src, int N, int p, int cb, int s,
+                                                    int e, h8v& hi, h8v& lo) {
+    const int col = cb * 16 + (g.lane & 15);
+    float v[8];
+    if (col < p) {
+      loadf8(src + (size_t)col * ((size_t)N + 4) + 32 * s + 8 * (g.lane >> 4), v);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = 0.f;
+    }
+    split8(v, e, hi, lo);
+  }
+
+  // One CholeskyQR pass src -> dst (N x p bases, column-major, N + 4 floats
+  // per column; dst's columns from p to pc become zero), to be followed by a
+  // barrier of the caller. Wavefront 0 forms the p x p Gram matrix of src 2^e
+  // on the matrix cores (split binary16, e from src's largest magnitude),
+  // factors it (lane i holds row i; columns reach the other lanes by readlane)
+  // and inverts the factor (lane c forms column c of L^-1); after a barrier
+  // every thread applies dst = 2^e src L^-T to its rows. A column whose
+  // remaining norm is below 1e-3 of its own (pivot below 1e-6 of its Gram
+  // diagonal) gets a zero row in L^-1 and drops out. Returns, in every thread,
+  // the ratio of the largest to the smallest live diagonal entry of L: an
+  // estimate of src's condition number. P16 is p rounded up to 16, P8 is p
+  // rounded up to a supported unrolled size.
+  template <int P16, int P8>
+  static __device__ __forceinline__ float orth_pass(const Geo& g, const MergeLayout& ML, const float* src, float* dst,
+                                                    int p, float* ws, float* misc) {
+    constexpr int NC = P16 / 16;
+    const int N = ML.N;
+    const size_t bs = (size_t)N + 4;
+    const int l = g.lane;
+    float* Lr = ws;                          // rows of L (and first the Gram matrix)
+    float* dinv = ws + kMaxCap * kWs;        // 1/L_ii (0 for a dropped column)
+    float* Mi = ws + (kMaxCap + 1) * kWs;    // rows of L^-1
+    if (g.wave == 0) {
+      const int e = fit_exp(basis_max<NC>(g, src, N, p));
+      // Gram blocks (a, b), a <= b: register r of lane l holds G[a*16 + 4(l/16) + r][b*16 + l%16]
+      f4v G[NC][NC];
+#pragma unroll
+      for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+        for (int b0 = 0; b0 < NC; ++b0) G[a0][b0] = f4v{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < N / 32; ++s) {
+        h8v hi[NC], lo[NC];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) basis_frag(g, src, N, p, cb, s, e, hi[cb], lo[cb]);
+#pragma unroll
+        for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+          for (int b0 = a0; b0 < NC; ++b0) {
+            G[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[a0], hi[b0], G[a0][b0], 0, 0, 0);
+            G[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi[a0], lo[b0], G[a0][b0], 0, 0, 0);
+            G[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo[a0], hi[b0], G[a0][b0], 0, 0, 0);
+          }
+      }
+      // to the scratch, row-major: every block exchanged (four consecutive
+      // columns per store), the off-diagonal ones also as they are
+#pragma unroll
+      for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+        for (int b0 = a0; b0 < NC; ++b0) {
+          *reinterpret_cast<f4v*>(Lr + (b0 * 16 + (l & 15)) * kWs + a0 * 16 + 4 * (l >> 4)) = G[a0][b0];
+          if (a0 < b0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Lr[(a0 * 16 + 4 * (l >> 4) + r) * kWs + b0 * 16 + (l & 15)] = G[a0][b0][r];
           }
         }
+      wave_sync_lds();
+      // G = L L^T, lane i holding row i
+      float row[P8];
+#pragma unroll
+      for (int c = 0; c < P8; ++c) row[c] = (l < p && c < p) ? Lr[l * kWs + c] : 0.f;
+      const float gii = (l < p) ? Lr[l * kWs + l] : 0.f;
+      float dmine = 0.f;
+#pragma unroll
+      for (int k = 0; k < P8; ++k) {
+        const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row[k]), k));
+        const float gkk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gii), k));
+        const bool live = piv > 1e-6f * gkk && piv > 0.f;
+        // 1/sqrt to about an ulp: the next pass (or CholeskyQR2) removes what this one leaves
+        const float di = live ? __builtin_amdgcn_rsqf(piv) : 0.f;
+        const float lik = __fmul_rn(row[k], di);
+        row[k] = lik;
+        if (l == k) dmine = di;
+#pragma unroll
+        for (int j = k + 1; j < P8; ++j) {
+          const float ljk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lik), j));
+          row[j] = __builtin_fmaf(-lik, ljk, row[j]);
+        }
       }
-      __syncthreads();
+      wave_sync_lds();   // every lane has read its Gram row
+      if (l < P8) {
+#pragma unroll
+        for (int c = 0; c < P8; c += 4)
+          *reinterpret_cast<f4v*>(Lr + l * kWs + c) = f4v{row[c], row[c + 1], row[c + 2], row[c + 3]};
+        dinv[l] = dmine;
+      }
+      wave_sync_lds();
+      // column l of L^-1: x_i = (i == l ? 1 : -sum_{t<i} L_it x_t) / L_ii, zero above l
+      if (l < P8) {
+        float x[P8];
+#pragma unroll
+        for (int i = 0; i < P8; ++i) {
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t4 = 0; t4 < i; t4 += 4) {
+            const f4v L4 = *reinterpret_cast<const f4v*>(Lr + i * kWs + t4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (t4 + t < i) s4[t] = __builtin_fmaf(L4[t], x[t4 + t], s4[t]);
+          }
+          const float su = __fadd_rn(__fadd_rn(s4[0], s4[1]), __fadd_rn(s4[2], s4[3]));
+          const float di = dinv[i];
+          x[i] = (i == l) ? di : ((i < l) ? 0.f : -__fmul_rn(di, su));
+          Mi[i * kWs + l] = x[i];
+        }
+      }
+      // condition estimate: the live diagonal entries of L are the 1/dinv
+      const bool lv = l < p && dmine > 0.f;
+      const float dmx = wave_max(lv ? dmine : 0.f);
+      const float dmn = -wave_max(lv ? -dmine : -INFINITY);
+      if (l == 0) {
+        misc[kMiscOrth] = (dmx > 0.f) ? dmx / dmn : 1.f;
+        misc[kMiscOrth + 1] = __int_as_float(e);
+      }
     }
+    __syncthreads();
+    const int e = __float_as_int(misc[kMiscOrth + 1]);
+    const float kappa = misc[kMiscOrth];
+    // dst = 2^e src L^-T: lane -> row, and a wavefront-uniform group of columns
+    // (c = gm, gm + G, ...) per wavefront, so that no lane idles on another's columns
+    const int nrg = (N + 63) / 64;           // row groups of 64
+    const int G = g.nw / nrg;                // column groups
+    const int gm = g.wave / nrg;
+    const int r = (g.wave - gm * nrg) * 64 + l;
+    uint32_t mine = 0;                       // this group's columns
+    for (int c = gm; c < P8; c += G) mine |= 1u << c;
+    if (gm < G && r < N) {
+      float yv[P8];
+#pragma unroll
+      for (int c = 0; c < P8; ++c) yv[c] = (c < p) ? ldexpf(src[(size_t)c * bs + r], e) : 0.f;
+#pragma unroll
+      for (int c = 0; c < P8; ++c) {
+        if (!((mine >> c) & 1u)) continue;   // wavefront-uniform
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t4 = 0; t4 <= c; t4 += 4) {
+          const f4v M4 = *reinterpret_cast<const f4v*>(Mi + c * kWs + t4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (t4 + t <= c) s4[t] = __builtin_fmaf(M4[t], yv[t4 + t], s4[t]);
+        }
+        dst[(size_t)c * bs + r] = (c < p) ? __fadd_rn(__fadd_rn(s4[0], s4[1]), __fadd_rn(s4[2], s4[3])) : 0.f;
+      }
+      if (gm == 0)
+        for (int c = P8; c < ML.pc; ++c) dst[(size_t)c * bs + r] = 0.f;
+    }
+    return kappa;
+  }
+
+  // H = Q^T Y (p x p, Y = C Q 2^kQScale) on the matrix cores in wavefront 0,
+  // symmetrised into h (row stride kSm), with `hs` as scratch. Returns E with
+  // H = 2^E Q^T C Q.
+  template <int P16>
+  static __device__ __forceinline__ int rr_matrix(const Geo& g, const MergeLayout& ML, const float* q, const float* y,
+                                                  int p, float* h, float* hs) {
+    constexpr int NC = P16 / 16;
+    const int N = ML.N;
+    const int l = g.lane;
+    const int ey = fit_exp(basis_max<NC>(g, y, N, p));
+    f4v H4[NC][NC];
+#pragma unroll
+    for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+      for (int b0 = 0; b0 < NC; ++b0) H4[a0][b0] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < N / 32; ++s) {
+      h8v qh[NC], ql[NC], yh[NC], yl[NC];
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) {
+        basis_frag(g, q, N, p, cb, s, kQScale, qh[cb], ql[cb]);
+        basis_frag(g, y, N, p, cb, s, ey, yh[cb], yl[cb]);
+      }
+#pragma unroll
+      for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+        for (int b0 = 0; b0 < NC; ++b0) {
+          H4[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[a0], yh[b0], H4[a0][b0], 0, 0, 0);
+          H4[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[a0], yl[b0], H4[a0][b0], 0, 0, 0);
+          H4[a0][b0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[a0], yh[b0], H4[a0][b0], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int a0 = 0; a0 < NC; ++a0)
+#pragma unroll
+      for (int b0 = 0; b0 < NC; ++b0)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hs[(a0 * 16 + 4 * (l >> 4) + r) * kSm + b0 * 16 + (l & 15)] = H4[a0][b0][r];
+    wave_sync_lds();
+    for (int e = l; e < p * p; e += 64) {
+      const int i = e / p, j = e - i * p;
+      h[i * kSm + j] = 0.5f * (hs[i * kSm + j] + hs[j * kSm + i]);
+    }
+    return 2 * kQScale + ey;
   }
 
   // Partner of index x in round r of the round-robin schedule for P (even)
@@ -493,86 +803,422 @@ struct Merge {
     return (y >= P - 1) ? y - (P - 1) : y;
   }
 
-  // Cyclic Jacobi on the symmetric p x p matrix in S.h0, all threads. Per
-  // round, the P/2 disjoint rotations of the round-robin schedule: one thread
-  // per rotation finds its angle and publishes J_xx, J_yx for both indices,
-  // then H <- J^T H J and V <- V J go element-wise into the other buffer. On
-  // return H points at the eigenvalues (diagonal) and V at the eigenvectors
-  // (columns).
-  static __device__ __forceinline__ void jacobi(const Geo& g, int p, float*& H, float*& V, float*& Hn, float*& Vn,
-                                                const MergeLds& S) {
-    for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
-      const int i = e / p, j = e - i * p;
-      V[i * kSm + j] = (i == j) ? 1.f : 0.f;
+  // cos and sin of the rotation that zeroes H_ab (a < b) given H_aa, H_bb, H_ab;
+  // index a gets (J_aa, J_ba) = (c, -sn) and b gets (J_bb, J_ab) = (c, sn)
+  static __device__ __forceinline__ void rot_cs(float haa, float hbb, float hab, float& c, float& sn) {
+    c = 1.f;
+    sn = 0.f;
+    if (hab != 0.f) {
+      // the angle to about an ulp: the rotations stay orthogonal to that order
+      const float th = (hbb - haa) * (0.5f * __builtin_amdgcn_rcpf(hab));
+      const float at = fabsf(th);
+      const float t = (at > 1e18f) ? 0.5f * __builtin_amdgcn_rcpf(th)
+                                   : copysignf(__builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(th * th + 1.f)), th);
+      c = __builtin_amdgcn_rsqf(t * t + 1.f);
+      sn = t * c;
     }
+  }
+
+  // Cyclic Jacobi on the symmetric p x p matrix at H (row stride kSm), all
+  // threads, one barrier per round. Round r applies the P/2 disjoint rotations
+  // of the round-robin schedule, whose coefficients and partners are in the
+  // table `rcur`: each thread writes its elements of J^T H J and V J into the
+  // other buffers, and the thread owning the element (a, b), a < b, that is a
+  // pair of the next round also forms the new H_aa and H_bb and publishes the
+  // next rotation of a and b (an index paired with the padding player gets the
+  // identity from its diagonal element's thread). The sweep stops at its start
+  // once the off-diagonal part's squared norm is below 1e-4 of the diagonal's
+  // (eigenvector errors of 1e-2 change the rank-k error only in the second
+  // order). On return H holds the eigenvalues on its diagonal and V the
+  // eigenvectors in its columns.
+  static __device__ __forceinline__ void jacobi(const Geo& g, int p, float*& H, float*& V, float*& Hn, float*& Vn,
+                                                float* misc, float4* rot) {
+    const int tid = threadIdx.x, nt = blockDim.x;
     const int P = (p + 1) & ~1;
-    float* flag = S.misc + kMiscFlag;
-    float* rot = S.misc + kMiscRot;   // [kMaxCap][2]: J_xx, J_(partner, x)
+    const int ne = p * p;
+    const bool two = ne > nt;   // p * p <= 2 * 512 always
+    int ei[2], ej[2];
+    bool own[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + u * nt;
+      own[u] = e < ne;
+      ei[u] = own[u] ? e / p : 0;
+      ej[u] = own[u] ? e - ei[u] * p : 0;
+    }
+    float4* rcur = rot;
+    float4* rnxt = rot + kMaxCap;
+    float off = 0.f, dia = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!own[u]) continue;
+      const int i = ei[u], j = ej[u];
+      V[i * kSm + j] = (i == j) ? 1.f : 0.f;
+      const float h = H[i * kSm + j];
+      if (i == j) dia = __builtin_fmaf(h, h, dia);
+      else off = __builtin_fmaf(h, h, off);
+      const int y = rr_partner(i, 0, P);
+      if (i == j && y >= p) rcur[i] = make_float4(1.f, 0.f, __int_as_float(i), 0.f);
+      if (i < j && y == j) {
+        float c, sn;
+        rot_cs(H[i * kSm + i], H[j * kSm + j], h, c, sn);
+        rcur[i] = make_float4(c, -sn, __int_as_float(j), 0.f);
+        rcur[j] = make_float4(c, sn, __int_as_float(i), 0.f);
+      }
+    }
+    off = wave_sum(off);
+    dia = wave_sum(dia);
+    if (g.lane == 0) {
+      misc[kMiscJac + 2 * g.wave] = off;
+      misc[kMiscJac + 2 * g.wave + 1] = dia;
+    }
     __syncthreads();
-    for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
-      if (g.wave == 0) {
-        float off = 0.f, dia = 0.f;
-        for (int e = g.lane; e < p * p; e += 64) {
-          const int i = e / p, j = e - i * p;
-          const float h = H[i * kSm + j];
-          if (i == j) dia = __builtin_fmaf(h, h, dia);
-          else off = __builtin_fmaf(h, h, off);
+    int round = 0, sweep = 0;
+    for (;;) {
+      if (round == 0) {
+        // the norms at the start of this sweep (double buffered by sweep parity)
+        const float* pb = misc + kMiscJac + (sweep & 1) * 16;
+        float so = 0.f, sd = 0.f;
+        for (int w = 0; w < g.nw; ++w) {
+          so += pb[2 * w];
+          sd += pb[2 * w + 1];
         }
-        off = wave_sum(off);
-        dia = wave_sum(dia);
-        // an off-diagonal norm of 1e-2 of the diagonal's leaves eigenvector
-        // errors of that order, whose effect on the rank-k error is of second
-        // order (about 1e-4 relative): on the GLA workload's residuals the
-        // excess over the Eckart-Young optimum is the same as with a 1e-4
-        // stop, one sweep earlier
-        if (g.lane == 0) flag[0] = (off <= 1e-4f * dia) ? 1.f : 0.f;
+        if (!(so > 1e-4f * sd) || sweep == kJacobiSweeps) break;   // (a NaN matrix stops too)
+      }
+      const int nxt = (round + 1 == P - 1) ? 0 : round + 1;
+      float off2 = 0.f, dia2 = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && !two) break;
+        if (!own[u]) continue;
+        const int i = ei[u], j = ej[u];
+        const float4 ri = rcur[i], rj = rcur[j];
+        const int pi = __float_as_int(ri.z), pj = __float_as_int(rj.z);
+        const float hn = ri.x * (rj.x * H[i * kSm + j] + rj.y * H[i * kSm + pj]) +
+                         ri.y * (rj.x * H[pi * kSm + j] + rj.y * H[pi * kSm + pj]);
+        Hn[i * kSm + j] = hn;
+        Vn[i * kSm + j] = rj.x * V[i * kSm + j] + rj.y * V[i * kSm + pj];
+        if (nxt == 0) {
+          if (i == j) dia2 = __builtin_fmaf(hn, hn, dia2);
+          else off2 = __builtin_fmaf(hn, hn, off2);
+        }
+        const int y = rr_partner(i, nxt, P);
+        if (i == j && y >= p) rnxt[i] = make_float4(1.f, 0.f, __int_as_float(i), 0.f);
+        if (i < j && y == j) {
+          // the pair's new diagonal entries, as their own threads form them
+          const float hii = ri.x * (ri.x * H[i * kSm + i] + ri.y * H[i * kSm + pi]) +
+                            ri.y * (ri.x * H[pi * kSm + i] + ri.y * H[pi * kSm + pi]);
+          const float hjj = rj.x * (rj.x * H[j * kSm + j] + rj.y * H[j * kSm + pj]) +
+                            rj.y * (rj.x * H[pj * kSm + j] + rj.y * H[pj * kSm + pj]);
+          float c, sn;
+          rot_cs(hii, hjj, hn, c, sn);
+          rnxt[i] = make_float4(c, -sn, __int_as_float(j), 0.f);
+          rnxt[j] = make_float4(c, sn, __int_as_float(i), 0.f);
+        }
+      }
+      if (nxt == 0) {
+        off2 = wave_sum(off2);
+        dia2 = wave_sum(dia2);
+        if (g.lane == 0) {
+          float* pb = misc + kMiscJac + ((sweep + 1) & 1) * 16;
+          pb[2 * g.wave] = off2;
+          pb[2 * g.wave + 1] = dia2;
+        }
       }
       __syncthreads();
-      if (flag[0] != 0.f) break;
-      for (int round = 0; round < P - 1; ++round) {
-        if ((int)threadIdx.x < p) {
-          const int x = threadIdx.x, y = rr_partner(x, round, P);
-          if (x < y) {
-            float c = 1.f, sn = 0.f;
-            if (y < p) {
-              const float haa = H[x * kSm + x], hbb = H[y * kSm + y], hab = H[x * kSm + y];
-              if (hab != 0.f) {
-                // the angle to about an ulp: the rotations stay orthogonal to that order
-                const float th = (hbb - haa) * (0.5f * __builtin_amdgcn_rcpf(hab));
-                const float at = fabsf(th);
-                const float t = (at > 1e18f) ? 0.5f * __builtin_amdgcn_rcpf(th)
-                                             : copysignf(__builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(th * th + 1.f)), th);
-                c = __builtin_amdgcn_rsqf(t * t + 1.f);
-                sn = t * c;
-              }
-            }
-            rot[2 * x] = c;
-            rot[2 * x + 1] = -sn;       // J_(y, x) = -s for the lower index
-            if (y < p) {
-              rot[2 * y] = c;
-              rot[2 * y + 1] = sn;      // J_(x, y) = s
-            }
-          } else if (y >= p) {
-            rot[2 * x] = 1.f;           // paired with the padding player
-            rot[2 * x + 1] = 0.f;
-          }
+      float* t = H; H = Hn; Hn = t;
+      t = V; V = Vn; Vn = t;
+      float4* tr = rcur; rcur = rnxt; rnxt = tr;
+      round = nxt;
+      if (round == 0) ++sweep;
+    }
+  }
+
+  static __device__ __forceinline__ float bperm(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(v)));
+  }
+
+  // Slot pairs and their rotation for the one-wavefront Jacobi: players of the
+  // round-robin schedule (circle method: position 0 fixed, positions 1 .. 15
+  // rotate by one per round, pairs (m, 15 - m)) sit in slots 2m (position m)
+  // and 2m + 1 (position 15 - m), so the pairs are always the slot pairs of the
+  // 2 x 2 blocks. From one round to the next, slot half (m, tau) (tau = 0 for
+  // slot 2m, 1 for 2m + 1) takes the player of rowmap(m, tau).
+  static __device__ __forceinline__ void rowmap(int m, int tau, int& m2, int& tau2) {
+    if (tau == 0) {
+      if (m == 0) { m2 = 0; tau2 = 0; }
+      else if (m == 1) { m2 = 0; tau2 = 1; }
+      else { m2 = m - 1; tau2 = 0; }
+    } else {
+      if (m < 7) { m2 = m + 1; tau2 = 1; }
+      else { m2 = 7; tau2 = 0; }
+    }
+  }
+
+  // Cyclic Jacobi on the symmetric p x p matrix at H (p <= 16, padded to 16
+  // with zeros), in wavefront 0 alone and in registers: lane L holds the 2 x 2
+  // blocks (L/8, L%8) of H and of V (V's rows are the basis index, its columns
+  // the slots). A round rotates every slot pair (2m, 2m+1) by the angle its
+  // diagonal block gives (the same rotation as the all-thread version's), then
+  // moves rows and columns of H and columns of V to the next round's slots by
+  // ds_bpermute. The sweep stops at its start once the off-diagonal part's
+  // squared norm is below 1e-4 of the diagonal's. On return H's diagonal holds
+  // the 16 slots' eigenvalues and V's columns their eigenvectors (padding
+  // slots: eigenvalue 0, eigenvector on a padding row).
+  static __device__ __forceinline__ void jacobi16(const Geo& g, int p, float* H, float* V) {
+    const int l = g.lane;
+    const int A = l >> 3, B = l & 7;
+    const bool dg = A == B;
+    float h[4], v[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = 2 * A + (d >> 1), c = 2 * B + (d & 1);
+      h[d] = (r < p && c < p) ? H[r * kSm + c] : 0.f;
+      v[d] = (r == c) ? 1.f : 0.f;
+    }
+    // where each register comes from after a round's rotation (fixed)
+    int hsl[4], hsr[4], vsl[4], vsr[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      int ra, rt, cb, ct;
+      rowmap(A, d >> 1, ra, rt);
+      rowmap(B, d & 1, cb, ct);
+      hsl[d] = 8 * ra + cb;
+      hsr[d] = 2 * rt + ct;
+      vsl[d] = 8 * A + cb;
+      vsr[d] = ct;
+    }
+    for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
+      float off = dg ? __fmaf_rn(h[1], h[1], h[2] * h[2])
+                     : __fmaf_rn(h[0], h[0], __fmaf_rn(h[1], h[1], __fmaf_rn(h[2], h[2], h[3] * h[3])));
+      float dia = dg ? __fmaf_rn(h[0], h[0], h[3] * h[3]) : 0.f;
+      off = wave_sum(off);
+      dia = wave_sum(dia);
+      if (!(off > 1e-4f * dia)) break;   // (a NaN matrix stops too)
+      for (int round = 0; round < 15; ++round) {
+        // the pair rotation of this lane's block row A and column B
+        float c, sn;
+        rot_cs(h[0], h[3], h[1], c, sn);   // meaningful on the diagonal blocks
+        const float cA = bperm(c, 9 * A), sA = bperm(sn, 9 * A);
+        const float cB = bperm(c, 9 * B), sB = bperm(sn, 9 * B);
+        // J = [[c, s], [-s, c]]: T = H J_B, H' = J_A^T T, V' = V J_B
+        const float t0 = h[0] * cB - h[1] * sB, t1 = h[0] * sB + h[1] * cB;
+        const float t2 = h[2] * cB - h[3] * sB, t3 = h[2] * sB + h[3] * cB;
+        float m[4];
+        m[0] = cA * t0 - sA * t2;
+        m[1] = cA * t1 - sA * t3;
+        m[2] = sA * t0 + cA * t2;
+        m[3] = sA * t1 + cA * t3;
+        if (dg) {   // the rotation zeroes the pair's off-diagonal element
+          m[1] = 0.f;
+          m[2] = 0.f;
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < p * p; e += blockDim.x) {
-          const int i = e / p, j = e - i * p;
-          int pi = rr_partner(i, round, P), pj = rr_partner(j, round, P);
-          pi = (pi < p) ? pi : i;
-          pj = (pj < p) ? pj : j;
-          const float2 ri = *reinterpret_cast<const float2*>(rot + 2 * i);
-          const float2 rj = *reinterpret_cast<const float2*>(rot + 2 * j);
-          Hn[i * kSm + j] = ri.x * (rj.x * H[i * kSm + j] + rj.y * H[i * kSm + pj]) +
-                            ri.y * (rj.x * H[pi * kSm + j] + rj.y * H[pi * kSm + pj]);
-          Vn[i * kSm + j] = rj.x * V[i * kSm + j] + rj.y * V[i * kSm + pj];
+        float w[4];
+        w[0] = v[0] * cB - v[1] * sB;
+        w[1] = v[0] * sB + v[1] * cB;
+        w[2] = v[2] * cB - v[3] * sB;
+        w[3] = v[2] * sB + v[3] * cB;
+        // to the next round's slots
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const float x0 = bperm(m[0], hsl[d]), x1 = bperm(m[1], hsl[d]);
+          const float x2 = bperm(m[2], hsl[d]), x3 = bperm(m[3], hsl[d]);
+          h[d] = hsr[d] == 0 ? x0 : (hsr[d] == 1 ? x1 : (hsr[d] == 2 ? x2 : x3));
+          const float y0 = bperm(w[2 * (d >> 1)], vsl[d]), y1 = bperm(w[2 * (d >> 1) + 1], vsl[d]);
+          v[d] = vsr[d] == 0 ? y0 : y1;
         }
-        __syncthreads();
-        float* t = H; H = Hn; Hn = t;
-        t = V; V = Vn; Vn = t;
       }
+    }
+    // eigenvalues on the diagonal, eigenvectors in the columns (slot order)
+    if (dg) {
+      H[(2 * A) * kSm + 2 * A] = h[0];
+      H[(2 * A + 1) * kSm + 2 * A + 1] = h[3];
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) V[(2 * A + (d >> 1)) * kSm + 2 * B + (d & 1)] = v[d];
+  }
+
+  // The rank-k factors of R (2^eR R split in X's area, R in registers),
+  // written to the bypass's first k columns as U_k S^1/2 and V_k S^1/2.
+  template <int P16, int P8>
+  static __device__ __forceinline__ void factor(const StepArgs& a, const Geo& g, const MergeLayout& ML,
+                                                const float R[8][8], float rmax, int p, int k, __half* U,
+                                                __half* W) {
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int N = ML.N;
+    const size_t bs = (size_t)N + 4;
+    float* misc = lds + ML.misc;
+    _Float16* lh = reinterpret_cast<_Float16*>(lds);
+    const int eR = fit_exp(rmax);
+    write_x(g, ML, R, eR, lh + ML.xh, lh + ML.xl);
+    __syncthreads();
+    f16v acc[4];
+    form_c(g, ML, lh + ML.xh, lh + ML.xl, acc);
+    __syncthreads();   // X's area becomes C's
+    // C' = X^T X <= K 2^30 entrywise; 2^eC C' <= 2^14 fits binary16 with its low part
+    const int eC = -(16 + (32 - __builtin_clz((unsigned)ML.K - 1u)));
+    _Float16* chh = lh + ML.ch;
+    _Float16* cll = lh + ML.cl;
+    store_c(g, ML, acc, eC, chh, cll);
+    // the start basis: the bypass's factors on the narrow side, which span L's
+    // row (or column) space; all of them are read before any is rewritten.
+    // Their largest magnitude sets the first product's binary16 scale.
+    float* Qb = lds + ML.q;
+    float* Yb = lds + ML.y;
+    float* wsc = lds + ML.ws;
+    const __half* F = ML.right ? W : U;
+    float fm = 0.f;
+    for (int e = tid; e < ML.pc * N; e += nt) {
+      const int c = e / N, r = e - c * N;
+      const float v = (c < p) ? __half2float(F[(size_t)c * N + r]) : 0.f;
+      Qb[(size_t)c * bs + r] = v;
+      fm = fmaxf(fm, fabsf(v));
+    }
+    fm = wave_max(fm);
+    if (g.lane == 0) misc[kMiscWave + g.wave] = fm;
+    __syncthreads();
+    for (int w = 0; w < g.nw; ++w) fm = fmaxf(fm, misc[kMiscWave + w]);
+    const int iters = (p >= 4 * k + 4) ? kMergeItersWide : (p >= 3 * k + 4) ? kMergeItersMid : kMergeItersNarrow;
+    float kappa = 1.f;
+    // (the non-finite flags' slots: read long before, many barriers back)
+    float* wmax = misc + kMiscWave + 8;
+    for (int it = 0; it < iters;) {
+      cq(g, ML, chh, cll, Qb, Yb, it == 0 ? fit_exp(fm) : kQScale, wmax);
+      __syncthreads();
+      ++it;
+      // a well-conditioned basis takes a second product before it is
+      // orthonormalised again: the condition number grows by at most the
+      // product's, about the last estimate (uniform: every thread read it)
+      if (it < iters && kappa <= 4.f) {
+        float ym = 0.f;
+        for (int w = 0; w < g.nw; ++w) ym = fmaxf(ym, wmax[w]);
+        __syncthreads();   // the maxima are read before the next product rewrites them
+        cq(g, ML, chh, cll, Yb, Qb, fit_exp(ym), wmax);
+        __syncthreads();
+        ++it;
+        float* t = Qb;
+        Qb = Yb;
+        Yb = t;
+      }
+      kappa = orth_pass<P16, P8>(g, ML, Yb, Qb, p, wsc, misc);
+      __syncthreads();
+    }
+    // CholeskyQR's loss of orthogonality grows like the square of the
+    // condition number times the Gram matrix's precision (about 2^-22 here):
+    // below 20 it stays under 1e-4, which changes the rank-k error by far
+    // less than its tolerance; above, a second pass (CholeskyQR2). Uniform:
+    // every thread read the same estimate.
+    if (!(kappa <= 20.f)) {
+      orth_pass<P16, P8>(g, ML, Qb, Yb, p, wsc, misc);
+      __syncthreads();
+      float* t = Qb;
+      Qb = Yb;
+      Yb = t;
+    }
+    // Rayleigh-Ritz on Q^T C Q
+    cq(g, ML, chh, cll, Qb, Yb, kQScale, wmax);
+    __syncthreads();
+    float* H = lds + ML.h0;
+    float* Hn = lds + ML.h1;
+    float* V = lds + ML.v0;
+    float* Vn = lds + ML.v1;
+    if (g.wave == 0) {
+      const int eh = rr_matrix<P16>(g, ML, Qb, Yb, p, H, Hn);
+      // H = 2^(eh + eC + 2 eR) Q^T R^T R Q (or R R^T)
+      if (g.lane == 0) misc[kMiscFlag + 1] = __int_as_float(eh + eC + 2 * eR);
+    }
+    __syncthreads();
+    // p <= 16: the one-wavefront Jacobi, whose 16 slots are ranked below
+    int pr = p;
+    if constexpr (P16 == 16) {
+      if (g.wave == 0) jacobi16(g, p, H, V);
+      __syncthreads();
+      pr = 16;
+    } else {
+      jacobi(g, p, H, V, Hn, Vn, misc, reinterpret_cast<float4*>(lds + ML.rot));
+    }
+    // order of the eigenvalues, largest first (ties by index)
+    int* order = reinterpret_cast<int*>(misc + kMiscOrder);
+    float* sroot = misc + kMiscSroot;
+    float* sinv = misc + kMiscSinv;
+    if (g.wave == 0 && g.lane < pr) {
+      // a NaN eigenvalue sorts last, so the ranks stay a permutation
+      auto key = [](float v) { return v == v ? v : -INFINITY; };
+      const float lam = key(H[g.lane * kSm + g.lane]);
+      int rank = 0;
+      for (int j = 0; j < pr; ++j) {
+        const float lj = key(H[j * kSm + j]);
+        rank += (lj > lam || (lj == lam && j < g.lane)) ? 1 : 0;
+      }
+      order[rank] = g.lane;
+    }
+    __syncthreads();
+    if (g.wave == 0 && g.lane < k) {
+      const int etot = __float_as_int(misc[kMiscFlag + 1]);
+      const float lam = ldexpf(H[order[g.lane] * kSm + order[g.lane]], -etot);   // sigma^2
+      const float sr = lam > 0.f ? __fsqrt_rn(__fsqrt_rn(lam)) : 0.f;              // sigma^(1/2)
+      sroot[g.lane] = sr;
+      sinv[g.lane] = sr > 0.f ? 1.0f / sr : 0.f;
+    }
+    // the narrow side's singular vectors v_m = Q V[:, order[m]] feed the
+    // product with R (C's area is free now)
+    MergeLds S;
+    S.zt = lds + ML.zt;
+    S.yt = lds + ML.yt;
+    S.part = lds + ML.part;
+    const int zs = merge_zs(a.dv), ys = merge_ys(a.dk);
+    float* nv = ML.right ? S.zt : S.yt;
+    const int ns = ML.right ? zs : ys;
+    for (int e = tid; e < k * N; e += nt) {
+      const int m = e / N, r = e - m * N;
+      const int oc = order[m];
+      float u = 0.f;
+      for (int c = 0; c < p; ++c) u = __builtin_fmaf(Qb[(size_t)c * bs + r], V[c * kSm + oc], u);
+      nv[(size_t)m * ns + r] = u;
+    }
+    __syncthreads();
+    // the other side: R v_m (d_k) or R^T v_m (d_v)
+    if (ML.right) prod_rz(a, g, R, S, k);
+    else prod_rty(a, g, R, S, k);
+    // U column m: (R v_m) sigma^-1/2 (v_m on the right) or v_m sigma^1/2; W column m the other way round
+    const float* uscale = ML.right ? sinv : sroot;
+    const float* wscale = ML.right ? sroot : sinv;
+    // sign of each U column: its largest-magnitude entry (first on ties) is positive
+    float* sgn = misc + kMiscSign;
+    for (int mcol = g.wave; mcol < k; mcol += g.nw) {
+      float best = -1.f, bval = 0.f;
+      int bidx = 0x7fffffff;
+      for (int i = g.lane; i < a.dk; i += 64) {
+        const float u = S.yt[(size_t)mcol * ys + i] * uscale[mcol];
+        // judged on the value as stored (binary16, whose rounding is odd-symmetric)
+        const float au = fabsf(__half2float(__float2half_rn(u)));
+        if (au > best || (au == best && i < bidx)) {
+          best = au;
+          bval = u;
+          bidx = i;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ob = __shfl_xor(best, m, 64), ov = __shfl_xor(bval, m, 64);
+        const int oi = __shfl_xor(bidx, m, 64);
+        if (ob > best || (ob == best && oi < bidx)) {
+          best = ob;
+          bval = ov;
+          bidx = oi;
+        }
+      }
+      if (g.lane == 0) sgn[mcol] = (bval < 0.f) ? -1.f : 1.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < k * a.dk; e += nt) {
+      const int m = e / a.dk, i = e - m * a.dk;
+      U[(size_t)m * a.dk + i] = __float2half_rn(sgn[m] * (S.yt[(size_t)m * ys + i] * uscale[m]));
+    }
+    for (int e = tid; e < k * a.dv; e += nt) {
+      const int m = e / a.dv, j = e - m * a.dv;
+      W[(size_t)m * a.dv + j] = __float2half_rn(sgn[m] * (S.zt[(size_t)m * zs + j] * wscale[m]));
     }
   }
 
@@ -584,131 +1230,71 @@ struct Merge {
     const HeadEntry he = head_entry(a, h);
     uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
     const Geo g = geo(a);
-    MergeLds S;
-    S.zt = lds;
-    S.yt = S.zt + (size_t)a.cap * merge_zs(a.dv);
-    S.part = S.yt + (size_t)a.cap * merge_ys(a.dk);
-    S.g = S.part + merge_part_floats(a.dk, a.dv, g.wrw, g.wcw, a.merge_chunk);
-    S.h0 = S.g + kMaxCap * kSm;
-    S.h1 = S.h0 + kMaxCap * kSm;
-    S.v0 = S.h1 + kMaxCap * kSm;
-    S.v1 = S.v0 + kMaxCap * kSm;
-    S.misc = S.v1 + kMaxCap * kSm;
+    const MergeLayout ML = merge_layout(a.dk, a.dv, g.wrw, g.wcw, a.cap, a.merge_chunk);
+    float* misc = lds + ML.misc;
 
     uint32_t flags = 0;
-    // the bypass factors go through LDS (the basis areas are free until the
-    // subspace iteration); L is formed once from them and kept for R
-    __half* us = reinterpret_cast<__half*>(S.yt);
-    __half* ws = reinterpret_cast<__half*>(S.zt);
-    stage_bypass(a, he, tb, us, ws);
+    // the bypass factors go through LDS; L is formed once from them and kept for R
+    __half* us = reinterpret_cast<__half*>(lds);
+    __half* wst = us + (size_t)a.n * a.dk;
+    stage_bypass(a, he, tb, us, wst);
     uint32_t mk[8];
     float R[8][8];   // L, kept through the requantization
     switch (he.bits) {
-      case 4: requantize<4>(a, he, tb, g, us, ws, mk, R, flags); break;
-      case 6: requantize<6>(a, he, tb, g, us, ws, mk, R, flags); break;
-      default: requantize<8>(a, he, tb, g, us, ws, mk, R, flags); break;
+      case 4: requantize<4>(a, he, tb, g, us, wst, mk, R, flags); break;
+      case 6: requantize<6>(a, he, tb, g, us, wst, mk, R, flags); break;
+      default: requantize<8>(a, he, tb, g, us, wst, mk, R, flags); break;
     }
-    // the residual R = L on the elements that stayed in the bypass
+    // the residual R = L on the elements that stayed in the bypass, its
+    // largest magnitude and whether it is finite
+    float am = 0.f;
+    bool bad = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 8; ++j) {
         if ((mk[i] >> j) & 0x101u) R[i][j] = 0.f;
-    __syncthreads();   // the staging area becomes the bases
+        const float v = fabsf(R[i][j]);
+        bad = bad || !(v <= 3.4e38f);
+        am = fmaxf(am, v);
+      }
+    am = wave_max(am);
+    const bool wbad = any_lane(bad);
+    if (g.lane == 0) {
+      misc[kMiscWave + g.wave] = am;
+      misc[kMiscWave + 8 + g.wave] = wbad ? 1.f : 0.f;
+    }
+    __syncthreads();   // the staging area is free; the maxima are out
+    float rmax = 0.f;
+    bool rbad = false;
+    for (int w = 0; w < g.nw; ++w) {
+      rmax = fmaxf(rmax, misc[kMiscWave + w]);
+      rbad = rbad || misc[kMiscWave + 8 + w] != 0.f;
+    }
+    if (rbad) flags |= kStatusNonfinite;
 
     const int p = a.n;
     const int k = min(a.lrb_k, p);
     __half* U = reinterpret_cast<__half*>(tb + he.bypass_u);
     __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
-    const int zs = merge_zs(a.dv), ys = merge_ys(a.dk);
-    float* H = S.h0;
-    float* Hn = S.h1;
-    float* V = S.v0;
-    float* Vn = S.v1;
-    if (k > 0) {
-      // start from the bypass's right factors (all of W is read before any of it is rewritten)
-      for (int e = threadIdx.x; e < p * a.dv; e += blockDim.x) {
-        const int c = e / a.dv, j = e - c * a.dv;
-        S.zt[(size_t)c * zs + j] = __half2float(W[(size_t)c * a.dv + j]);
-      }
-      __syncthreads();
-      const int iters = (p >= 4 * k + 4) ? kMergeItersWide : kMergeItersNarrow;
-      // Z needs no orthonormalisation of its own: span(R Z) does not depend
-      // on the basis of span(Z), and Q = orth(R Z) keeps the numbers in range
-      for (int it = 0; it < iters; ++it) {
-        prod_rz(a, g, R, S, p);
-        // one CholeskyQR pass keeps an intermediate basis well conditioned;
-        // the final one, which the factors are built from, gets two
-        orth(g, S.yt, ys, a.dk, p, S, it + 1 < iters ? 1 : 2);
-        prod_rty(a, g, R, S, p);
-      }
-      // Rayleigh-Ritz: B = Q^T R = Z^T, B B^T = Z^T Z
-      gram(g, S.zt, zs, a.dv, p, H, S.part);
-      jacobi(g, p, H, V, Hn, Vn, S);
-      // order of the eigenvalues, largest first (ties by index)
-      int* order = reinterpret_cast<int*>(S.misc + kMiscOrder);
-      float* sroot = S.misc + kMiscSroot;
-      if (g.wave == 0 && g.lane < p) {
-        // a NaN eigenvalue sorts last, so the ranks stay a permutation
-        auto key = [](float v) { return v == v ? v : -INFINITY; };
-        const float lam = key(H[g.lane * kSm + g.lane]);
-        int rank = 0;
-        for (int j = 0; j < p; ++j) {
-          const float lj = key(H[j * kSm + j]);
-          rank += (lj > lam || (lj == lam && j < g.lane)) ? 1 : 0;
-        }
-        order[rank] = g.lane;
-      }
-      __syncthreads();
-      if (g.wave == 0 && g.lane < k) {
-        const float lam = H[order[g.lane] * kSm + order[g.lane]];
-        sroot[g.lane] = lam > 0.f ? __fsqrt_rn(__fsqrt_rn(lam)) : 0.f;   // sigma^(1/2)
-      }
-      __syncthreads();
-      // sign of each U column: its largest-magnitude entry (first on ties) is positive
-      float* sgn = S.misc + kMiscSign;
-      for (int mcol = g.wave; mcol < k; mcol += g.nw) {
-        const int oc = order[mcol];
-        float best = -1.f, bval = 0.f;
-        int bidx = 0x7fffffff;
-        for (int i = g.lane; i < a.dk; i += 64) {
-          float u = 0.f;
-          for (int c = 0; c < p; ++c) u = __builtin_fmaf(S.yt[(size_t)c * ys + i], V[c * kSm + oc], u);
-          // judged on the value as stored (binary16, whose rounding is odd-symmetric)
-          const float au = fabsf(__half2float(__float2half_rn(u * sroot[mcol])));
-          if (au > best || (au == best && i < bidx)) { best = au; bval = u; bidx = i; }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-          const float ob = __shfl_xor(best, m, 64), ov = __shfl_xor(bval, m, 64);
-          const int oi = __shfl_xor(bidx, m, 64);
-          if (ob > best || (ob == best && oi < bidx)) { best = ob; bval = ov; bidx = oi; }
-        }
-        if (g.lane == 0) sgn[mcol] = (bval < 0.f) ? -1.f : 1.f;
-      }
-      __syncthreads();
-      // U_k S^1/2 = Q V_k S^1/2 and V_k S^1/2 = Z V_k S^-1/2, rounded to binary16
-      for (int e = threadIdx.x; e < k * a.dk; e += blockDim.x) {
-        const int mcol = e / a.dk, i = e - mcol * a.dk;
-        const int oc = order[mcol];
-        float u = 0.f;
-        for (int c = 0; c < p; ++c) u = __builtin_fmaf(S.yt[(size_t)c * ys + i], V[c * kSm + oc], u);
-        U[(size_t)mcol * a.dk + i] = __float2half_rn(sgn[mcol] * (u * sroot[mcol]));
-      }
-      for (int e = threadIdx.x; e < k * a.dv; e += blockDim.x) {
-        const int mcol = e / a.dv, j = e - mcol * a.dv;
-        const int oc = order[mcol];
-        float w = 0.f;
-        for (int c = 0; c < p; ++c) w = __builtin_fmaf(S.zt[(size_t)c * zs + j], V[c * kSm + oc], w);
-        const float sr = sroot[mcol];
-        W[(size_t)mcol * a.dv + j] = __float2half_rn(sr > 0.f ? sgn[mcol] * (w / sr) : 0.f);
-      }
+    // a zero residual keeps zero factors; a non-finite one is flagged and dropped
+    const int kf = (rmax > 0.f && !rbad) ? k : 0;
+    // up to 8 kept columns the subspace iteration starts from at most 16 of
+    // the bypass's columns (the first ones: the previous merge's factors
+    // first), which keeps its small matrices to one wavefront
+    const int pb = (k <= 8 && p > 16) ? 16 : p;
+    if (kf > 0) {
+      if (pb <= 8) factor<16, 8>(a, g, ML, R, rmax, pb, k, U, W);
+      else if (pb <= 16) factor<16, 16>(a, g, ML, R, rmax, pb, k, U, W);
+      else if (pb <= 20) factor<32, 20>(a, g, ML, R, rmax, pb, k, U, W);
+      else if (pb <= 24) factor<32, 24>(a, g, ML, R, rmax, pb, k, U, W);
+      else factor<32, 32>(a, g, ML, R, rmax, pb, k, U, W);
     }
-    // the columns past k are empty
-    for (int e = threadIdx.x; e < (a.cap - k) * a.dk; e += blockDim.x)
-      U[(size_t)k * a.dk + e] = __float2half_rn(0.f);
-    for (int e = threadIdx.x; e < (a.cap - k) * a.dv; e += blockDim.x)
-      W[(size_t)k * a.dv + e] = __float2half_rn(0.f);
+    // the columns past the kept factors are empty
+    for (int e = threadIdx.x; e < (a.cap - kf) * a.dk; e += blockDim.x)
+      U[(size_t)kf * a.dk + e] = __float2half_rn(0.f);
+    for (int e = threadIdx.x; e < (a.cap - kf) * a.dv; e += blockDim.x)
+      W[(size_t)kf * a.dv + e] = __float2half_rn(0.f);
 
     if (any_lane(flags != 0)) {
 #pragma unroll
@@ -718,6 +1304,7 @@ struct Merge {
     if (tile == 0 && threadIdx.x == 0) *a.hdr_n = a.lrb_k;
   }
 };
+
 
 template <int CL>
 __global__ __launch_bounds__(512) void merge_kernel(StepArgs a) {
