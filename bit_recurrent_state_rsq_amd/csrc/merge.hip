@@ -79,13 +79,20 @@ __host__ __device__ inline size_t merge_part_floats(int dk, int dv, int wrw, int
 // in time; only `misc` lies outside it:
 //   staging       the bypass factors (binary16)
 //   phase B       X split: binary16 high and low planes, column-major, K + 8 halves per column
-//   phase C       q, y (bases, column-major, N + 4 floats per column), the split C
-//                 (row-major, N + 8 halves per row), the Gram / Cholesky scratch
-//   phase D       q (the final basis), the Jacobi buffers and rotations over C, then the closing
-//                 products' bases and partial sums
+//   C             the split Gram matrix (row-major, N + 8 halves per row): kept
+//                 through phase C, or (`creg`) only until every wavefront has
+//                 loaded its rows' MFMA fragments into registers
+//   phase C       q, y (bases, column-major, N + 4 floats per column), the Gram /
+//                 Cholesky scratch (after C when C stays)
+//   phase D       q (the final basis), the Jacobi buffers and rotations, the
+//                 closing products' bases and partial sums
+// `creg` holds when at most 8 columns are kept (the basis then has at most 16
+// columns, one MFMA column block) and every wavefront owns at most two of
+// C's 16-row blocks.
 struct MergeLayout {
-  int N, K, pc;       // narrow side, wide side, basis columns rounded up to 16
+  int N, K, pc;       // narrow side, wide side, basis columns (a multiple of 16)
   bool right;         // N = d_v: C = R^T R (else C = R R^T)
+  bool creg;          // C's fragments live in registers during the iteration
   size_t xh, xl;      // split X (halves)
   size_t ch, cl;      // split C (halves)
   size_t q, y, ws;    // bases; the Gram / Cholesky scratch
@@ -94,13 +101,14 @@ struct MergeLayout {
   size_t misc, total;
 };
 
-__host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int wcw, int cap, int chunk) {
+__host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int wcw, int cap, int k, int chunk) {
   MergeLayout L;
   L.right = dv <= dk;
   L.N = L.right ? dv : dk;
   L.K = L.right ? dk : dv;
-  L.pc = (cap + 15) & ~15;
   const int nw = wrw * wcw;
+  L.creg = k <= 8 && ((L.N / 16) + nw - 1) / nw <= 2;
+  L.pc = L.creg ? 16 : (cap + 15) & ~15;
   const size_t bs = (size_t)L.pc * (L.N + 4);
   const size_t csz = (size_t)L.N * (L.N + 8);   // two binary16 planes = one float per element
   const size_t stage = ((size_t)cap * (dk + dv) + 1) / 2;
@@ -109,9 +117,10 @@ __host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int
   L.xl = (size_t)L.N * (L.K + 8);
   L.q = 0;
   L.y = bs;
-  L.ch = 2 * (2 * bs);
+  const size_t c0 = L.creg ? 0 : 2 * bs;          // C (floats)
+  L.ch = 2 * c0;
   L.cl = L.ch + (size_t)L.N * (L.N + 8);
-  L.ws = 2 * bs + csz;
+  L.ws = L.creg ? 2 * bs : 2 * bs + csz;
   L.h0 = 2 * bs;
   L.h1 = L.h0 + kMaxCap * kSm;
   L.v0 = L.h1 + kMaxCap * kSm;
@@ -121,10 +130,10 @@ __host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int
   L.yt = L.zt + (size_t)cap * merge_zs(dv);
   L.part = L.yt + (size_t)cap * merge_ys(dk);
   const size_t phase_c = L.ws + kWsFloats;
-  (void)nw;
   const size_t phase_d = L.part + merge_part_floats(dk, dv, wrw, wcw, chunk);
   size_t u = stage;
   u = u > xsz ? u : xsz;
+  u = u > c0 + csz ? u : c0 + csz;
   u = u > phase_c ? u : phase_c;
   u = u > phase_d ? u : phase_d;
   L.misc = (u + 3) & ~size_t(3);
@@ -132,8 +141,8 @@ __host__ __device__ inline MergeLayout merge_layout(int dk, int dv, int wrw, int
   return L;
 }
 
-size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int chunk) {
-  return merge_layout(dk, dv, wrw, wcw, cap, chunk).total;
+size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int k, int chunk) {
+  return merge_layout(dk, dv, wrw, wcw, cap, k, chunk).total;
 }
 
 // the closing products' view of the LDS (the register products with R)
@@ -565,6 +574,74 @@ struct Merge {
     if (l == 0) wmax[g.wave] = m;
   }
 
+  // a fixed pseudo-random sign for (row, column) (an integer hash's low bit)
+  static __device__ __forceinline__ float pm1(int r, int c) {
+    uint32_t h = (uint32_t)r * 0x9E3779B1u ^ (uint32_t)c * 0x85EBCA77u;
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    return (h & 1u) ? 1.f : -1.f;
+  }
+
+  // This wavefront's A fragments of C (creg layouts): its 16-row blocks
+  // rb = wave + i * nw (i < 2), K steps s < N / 32 <= 4, high and low parts
+  struct CFrag {
+    h8v h[2][4], l[2][4];
+  };
+
+  static __device__ __forceinline__ void load_cfrag(const Geo& g, const MergeLayout& ML, const _Float16* chh,
+                                                    const _Float16* cll, CFrag& F) {
+    const int N = ML.N, nbr = N / 16;
+    const size_t cs = (size_t)N + 8;
+    const int l = g.lane;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rb = g.wave + i * g.nw;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (rb < nbr && s < N / 32) {
+          const size_t at = (size_t)(rb * 16 + (l & 15)) * cs + 32 * s + 8 * (l >> 4);
+          F.h[i][s] = *reinterpret_cast<const h8v*>(chh + at);
+          F.l[i][s] = *reinterpret_cast<const h8v*>(cll + at);
+        }
+      }
+    }
+  }
+
+  // cq with C's fragments in registers (creg: one 16-column block)
+  static __device__ __forceinline__ void cq_reg(const Geo& g, const MergeLayout& ML, const CFrag& F, const float* q,
+                                                float* y, int qe, float* wmax) {
+    const int N = ML.N, nbr = N / 16;
+    const size_t bs = (size_t)N + 4;
+    const int l = g.lane;
+    const float* qc = q + (size_t)(l & 15) * bs + 8 * (l >> 4);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rb = g.wave + i * g.nw;
+      if (rb < nbr) {
+        f4v acc = {};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s < N / 32) {
+            float v[8];
+            loadf8(qc + 32 * s, v);
+            h8v b_h, b_l;
+            split8(v, qe, b_h, b_l);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.h[i][s], b_h, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.h[i][s], b_l, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.l[i][s], b_h, acc, 0, 0, 0);
+          }
+        }
+        *reinterpret_cast<f4v*>(y + (size_t)(l & 15) * bs + rb * 16 + 4 * (l >> 4)) = acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[r]));
+      }
+    }
+    m = wave_max(m);
+    if (l == 0) wmax[g.wave] = m;
+  }
+
   // Largest magnitude over the lane's fragments of a basis (columns < p) and
   // its wavefront maximum
   template <int NC>
@@ -836,23 +913,13 @@ struct Merge {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int P = (p + 1) & ~1;
     const int ne = p * p;
-    const bool two = ne > nt;   // p * p <= 2 * 512 always
-    int ei[2], ej[2];
-    bool own[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + u * nt;
-      own[u] = e < ne;
-      ei[u] = own[u] ? e / p : 0;
-      ej[u] = own[u] ? e - ei[u] * p : 0;
-    }
     float4* rcur = rot;
     float4* rnxt = rot + kMaxCap;
     float off = 0.f, dia = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (!own[u]) continue;
-      const int i = ei[u], j = ej[u];
+    // the elements e = tid, tid + nt, ... of the p x p matrices (one per thread
+    // on the large blocks; the stride covers blocks of fewer threads)
+    for (int e = tid; e < ne; e += nt) {
+      const int i = e / p, j = e - (e / p) * p;
       V[i * kSm + j] = (i == j) ? 1.f : 0.f;
       const float h = H[i * kSm + j];
       if (i == j) dia = __builtin_fmaf(h, h, dia);
@@ -887,11 +954,8 @@ struct Merge {
       }
       const int nxt = (round + 1 == P - 1) ? 0 : round + 1;
       float off2 = 0.f, dia2 = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (u == 1 && !two) break;
-        if (!own[u]) continue;
-        const int i = ei[u], j = ej[u];
+      for (int e = tid; e < ne; e += nt) {
+        const int i = e / p, j = e - (e / p) * p;
         const float4 ri = rcur[i], rj = rcur[j];
         const int pi = __float_as_int(ri.z), pj = __float_as_int(rj.z);
         const float hn = ri.x * (rj.x * H[i * kSm + j] + rj.y * H[i * kSm + pj]) +
@@ -1061,21 +1125,41 @@ struct Merge {
     _Float16* chh = lh + ML.ch;
     _Float16* cll = lh + ML.cl;
     store_c(g, ML, acc, eC, chh, cll);
+    CFrag cf;
+    if (ML.creg) {
+      // every wavefront takes its rows of C into registers; then C's area is free
+      __syncthreads();
+      load_cfrag(g, ML, chh, cll, cf);
+      __syncthreads();
+    }
     // the start basis: the bypass's factors on the narrow side, which span L's
     // row (or column) space; all of them are read before any is rewritten.
-    // Their largest magnitude sets the first product's binary16 scale.
+    // An all-zero column (the slot of an earlier merge's empty residual) would
+    // leave the basis short of rank, so it gets a fixed pseudo-random +-1
+    // pattern instead. The largest magnitude sets the first product's binary16
+    // scale. Wavefront w takes columns w, w + nw, ... (N <= 128: two rows per lane).
     float* Qb = lds + ML.q;
     float* Yb = lds + ML.y;
     float* wsc = lds + ML.ws;
     const __half* F = ML.right ? W : U;
     float fm = 0.f;
-    for (int e = tid; e < ML.pc * N; e += nt) {
-      const int c = e / N, r = e - c * N;
-      const float v = (c < p) ? __half2float(F[(size_t)c * N + r]) : 0.f;
-      Qb[(size_t)c * bs + r] = v;
-      fm = fmaxf(fm, fabsf(v));
+    for (int c = g.wave; c < ML.pc; c += g.nw) {
+      const int r0 = g.lane, r1 = g.lane + 64;
+      float v0 = 0.f, v1 = 0.f;
+      if (c < p) {
+        if (r0 < N) v0 = __half2float(F[(size_t)c * N + r0]);
+        if (r1 < N) v1 = __half2float(F[(size_t)c * N + r1]);
+      }
+      float cm = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+      if (c < p && !(cm > 0.f)) {
+        v0 = pm1(r0, c);
+        v1 = pm1(r1, c);
+        cm = 1.f;
+      }
+      if (r0 < N) Qb[(size_t)c * bs + r0] = v0;
+      if (r1 < N) Qb[(size_t)c * bs + r1] = v1;
+      fm = fmaxf(fm, cm);
     }
-    fm = wave_max(fm);
     if (g.lane == 0) misc[kMiscWave + g.wave] = fm;
     __syncthreads();
     for (int w = 0; w < g.nw; ++w) fm = fmaxf(fm, misc[kMiscWave + w]);
@@ -1084,7 +1168,8 @@ struct Merge {
     // (the non-finite flags' slots: read long before, many barriers back)
     float* wmax = misc + kMiscWave + 8;
     for (int it = 0; it < iters;) {
-      cq(g, ML, chh, cll, Qb, Yb, it == 0 ? fit_exp(fm) : kQScale, wmax);
+      if (ML.creg) cq_reg(g, ML, cf, Qb, Yb, it == 0 ? fit_exp(fm) : kQScale, wmax);
+      else cq(g, ML, chh, cll, Qb, Yb, it == 0 ? fit_exp(fm) : kQScale, wmax);
       __syncthreads();
       ++it;
       // a well-conditioned basis takes a second product before it is
@@ -1094,7 +1179,8 @@ struct Merge {
         float ym = 0.f;
         for (int w = 0; w < g.nw; ++w) ym = fmaxf(ym, wmax[w]);
         __syncthreads();   // the maxima are read before the next product rewrites them
-        cq(g, ML, chh, cll, Yb, Qb, fit_exp(ym), wmax);
+        if (ML.creg) cq_reg(g, ML, cf, Yb, Qb, fit_exp(ym), wmax);
+        else cq(g, ML, chh, cll, Yb, Qb, fit_exp(ym), wmax);
         __syncthreads();
         ++it;
         float* t = Qb;
@@ -1117,7 +1203,8 @@ struct Merge {
       Yb = t;
     }
     // Rayleigh-Ritz on Q^T C Q
-    cq(g, ML, chh, cll, Qb, Yb, kQScale, wmax);
+    if (ML.creg) cq_reg(g, ML, cf, Qb, Yb, kQScale, wmax);
+    else cq(g, ML, chh, cll, Qb, Yb, kQScale, wmax);
     __syncthreads();
     float* H = lds + ML.h0;
     float* Hn = lds + ML.h1;
@@ -1230,7 +1317,7 @@ struct Merge {
     const HeadEntry he = head_entry(a, h);
     uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
     const Geo g = geo(a);
-    const MergeLayout ML = merge_layout(a.dk, a.dv, g.wrw, g.wcw, a.cap, a.merge_chunk);
+    const MergeLayout ML = merge_layout(a.dk, a.dv, g.wrw, g.wcw, a.cap, a.lrb_k, a.merge_chunk);
     float* misc = lds + ML.misc;
 
     uint32_t flags = 0;

@@ -177,18 +177,11 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64) +
                    (p.bypass ? rsq::kMaxCap + c->d_v : 0)) *
           sizeof(float);
-  // the merge reduces its products over as many basis columns per pass as
-  // the LDS holds (fewer passes, fewer barriers); at least 8
+  // the merge's closing products with R take 8 columns per pass (at most 8
+  // columns are kept in the common case), which keeps its LDS small enough
+  // for two tiles per compute unit on 128 x 128 heads
   G.merge_chunk = 8;
-  G.lds_merge = p.bypass ? rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap, 8) * sizeof(float) : 0;
-  if (p.bypass) {
-    for (int ch = 16; ch <= 32 && ch - 8 < p.cap; ch += 8) {
-      const size_t b = rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap, ch) * sizeof(float);
-      if (b > kLdsBytes) break;
-      G.merge_chunk = ch;
-      G.lds_merge = b;
-    }
-  }
+  G.lds_merge = p.bypass ? rsq::merge_lds_floats(c->d_k, c->d_v, G.wrw, G.wcw, p.cap, c->lrb_k, 8) * sizeof(float) : 0;
   if (G.lds_merge > kLdsBytes)
     return fail(RSQ_E_UNSUPPORTED, "the bypass merge of a %d x %d tile with %d columns needs %zu bytes of LDS",
                 c->d_k, c->d_v, p.cap, G.lds_merge);

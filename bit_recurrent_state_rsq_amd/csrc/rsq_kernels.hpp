@@ -49,8 +49,7 @@ struct StepArgs {
   int32_t uniform;
   uint64_t uni_stride;
   HeadEntry uni;
-  // bypass merge: basis columns per product pass (the host takes the
-  // largest of 8, 16, 24, 32 whose partial sums fit the LDS)
+  // bypass merge: columns per pass of its closing products with R
   int32_t merge_chunk;
 };
 
@@ -71,9 +70,9 @@ DecodeFn decode_boost_twin(DecodeFn fn);
 DecodeFn readout_kernel_for(int cl);
 DecodeFn merge_kernel_for(int cl);
 // dynamic LDS (floats) of the merge kernel for a tile of d_k x d_v split into
-// wrw x wcw wavefronts with `cap` bypass columns, reducing products over
-// `chunk` basis columns per pass
-size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int chunk);
+// wrw x wcw wavefronts with `cap` bypass columns of which k are kept,
+// reducing its closing products over `chunk` columns per pass
+size_t merge_lds_floats(int dk, int dv, int wrw, int wcw, int cap, int k, int chunk);
 
 // Decay of key row i of a tile (Table 1, A_t column).
 __device__ __forceinline__ float row_decay(const StepArgs& a, const HeadEntry& he, int model,

@@ -326,6 +326,10 @@ def test_cfg3_gla_full_horizon_with_merges():
     # the bypass column loop: one wavefront with more than four columns, and d_k > 256
     ("gla", 4, 64, "dynamic", "f16", 64, 64, 2, 6, True),
     ("retnet", 4, 32, "dynamic", "f16", 512, 32, 2, 3, False),
+    # more than 8 kept columns: the basis keeps all 17 - 32 bypass columns and
+    # Rayleigh-Ritz runs on all threads (two sizes of its unrolled factor)
+    ("gla", 4, 32, "dynamic", "f16", 128, 64, 9, 12, True),
+    ("gla", 4, 32, "dynamic", "f16", 128, 64, 10, 8, True),
 ])
 def test_merge_variants(model, bits, g, mode, sdt, dk, dv, k, m, bdr):
     base = {"retnet": CONFIGS[0], "mamba2": CONFIGS[2], "gla": CONFIGS[3]}[model]
