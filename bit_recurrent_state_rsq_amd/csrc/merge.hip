@@ -1024,12 +1024,15 @@ struct Merge {
   // blocks (L/8, L%8) of H and of V (V's rows are the basis index, its columns
   // the slots). A round rotates every slot pair (2m, 2m+1) by the angle its
   // diagonal block gives (the same rotation as the all-thread version's), then
-  // moves rows and columns of H and columns of V to the next round's slots by
-  // ds_bpermute. The sweep stops at its start once the off-diagonal part's
-  // squared norm is below 1e-4 of the diagonal's. On return H's diagonal holds
-  // the 16 slots' eigenvalues and V's columns their eigenvectors (padding
-  // slots: eigenvalue 0, eigenvector on a padding row).
-  static __device__ __forceinline__ void jacobi16(const Geo& g, int p, float* H, float* V) {
+  // moves rows and columns of H and columns of V to the next round's slots
+  // through the scratch `hs`, `vs` ([64][4] floats each): one store of every
+  // rotated block, then one batch of loads that brings each lane its new
+  // blocks and the new diagonal blocks of its pairs, from which it forms both
+  // of its next rotations itself. The sweep stops at its start once the
+  // off-diagonal part's squared norm is below 1e-4 of the diagonal's. On
+  // return H's diagonal holds the 16 slots' eigenvalues and V's columns their
+  // eigenvectors (padding slots: eigenvalue 0, eigenvector on a padding row).
+  static __device__ __forceinline__ void jacobi16(const Geo& g, int p, float* H, float* V, float* hs, float* vs) {
     const int l = g.lane;
     const int A = l >> 3, B = l & 7;
     const bool dg = A == B;
@@ -1040,17 +1043,34 @@ struct Merge {
       h[d] = (r < p && c < p) ? H[r * kSm + c] : 0.f;
       v[d] = (r == c) ? 1.f : 0.f;
     }
-    // where each register comes from after a round's rotation (fixed)
-    int hsl[4], hsr[4], vsl[4], vsr[4];
+    auto hp = [&](int r, int c) { return (r < p && c < p) ? H[r * kSm + c] : 0.f; };
+    // this round's rotations of pairs A and B, from their diagonal blocks
+    float cA, sA, cB, sB;
+    rot_cs(hp(2 * A, 2 * A), hp(2 * A + 1, 2 * A + 1), hp(2 * A, 2 * A + 1), cA, sA);
+    rot_cs(hp(2 * B, 2 * B), hp(2 * B + 1, 2 * B + 1), hp(2 * B, 2 * B + 1), cB, sB);
+    // where each value comes from after a round (fixed): own block's four H
+    // and four V values, and the new diagonal blocks (aa, bb, ab) of A and B
+    int hsrc[4], vsrc[4], dA[3], dB[3];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       int ra, rt, cb, ct;
       rowmap(A, d >> 1, ra, rt);
       rowmap(B, d & 1, cb, ct);
-      hsl[d] = 8 * ra + cb;
-      hsr[d] = 2 * rt + ct;
-      vsl[d] = 8 * A + cb;
-      vsr[d] = ct;
+      hsrc[d] = 4 * (8 * ra + cb) + 2 * rt + ct;
+      vsrc[d] = 4 * (8 * A + cb) + 2 * (d >> 1) + ct;
+    }
+    {
+      int r0, t0, r1, t1;
+      rowmap(A, 0, r0, t0);
+      rowmap(A, 1, r1, t1);
+      dA[0] = 4 * (8 * r0 + r0) + 2 * t0 + t0;
+      dA[1] = 4 * (8 * r1 + r1) + 2 * t1 + t1;
+      dA[2] = 4 * (8 * r0 + r1) + 2 * t0 + t1;
+      rowmap(B, 0, r0, t0);
+      rowmap(B, 1, r1, t1);
+      dB[0] = 4 * (8 * r0 + r0) + 2 * t0 + t0;
+      dB[1] = 4 * (8 * r1 + r1) + 2 * t1 + t1;
+      dB[2] = 4 * (8 * r0 + r1) + 2 * t0 + t1;
     }
     for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
       float off = dg ? __fmaf_rn(h[1], h[1], h[2] * h[2])
@@ -1060,15 +1080,10 @@ struct Merge {
       dia = wave_sum(dia);
       if (!(off > 1e-4f * dia)) break;   // (a NaN matrix stops too)
       for (int round = 0; round < 15; ++round) {
-        // the pair rotation of this lane's block row A and column B
-        float c, sn;
-        rot_cs(h[0], h[3], h[1], c, sn);   // meaningful on the diagonal blocks
-        const float cA = bperm(c, 9 * A), sA = bperm(sn, 9 * A);
-        const float cB = bperm(c, 9 * B), sB = bperm(sn, 9 * B);
         // J = [[c, s], [-s, c]]: T = H J_B, H' = J_A^T T, V' = V J_B
         const float t0 = h[0] * cB - h[1] * sB, t1 = h[0] * sB + h[1] * cB;
         const float t2 = h[2] * cB - h[3] * sB, t3 = h[2] * sB + h[3] * cB;
-        float m[4];
+        f4v m, w;
         m[0] = cA * t0 - sA * t2;
         m[1] = cA * t1 - sA * t3;
         m[2] = sA * t0 + cA * t2;
@@ -1077,20 +1092,24 @@ struct Merge {
           m[1] = 0.f;
           m[2] = 0.f;
         }
-        float w[4];
         w[0] = v[0] * cB - v[1] * sB;
         w[1] = v[0] * sB + v[1] * cB;
         w[2] = v[2] * cB - v[3] * sB;
         w[3] = v[2] * sB + v[3] * cB;
-        // to the next round's slots
+        *reinterpret_cast<f4v*>(hs + 4 * l) = m;
+        *reinterpret_cast<f4v*>(vs + 4 * l) = w;
+        wave_sync_lds();
+        // the next round's slots
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          const float x0 = bperm(m[0], hsl[d]), x1 = bperm(m[1], hsl[d]);
-          const float x2 = bperm(m[2], hsl[d]), x3 = bperm(m[3], hsl[d]);
-          h[d] = hsr[d] == 0 ? x0 : (hsr[d] == 1 ? x1 : (hsr[d] == 2 ? x2 : x3));
-          const float y0 = bperm(w[2 * (d >> 1)], vsl[d]), y1 = bperm(w[2 * (d >> 1) + 1], vsl[d]);
-          v[d] = vsr[d] == 0 ? y0 : y1;
+          h[d] = hs[hsrc[d]];
+          v[d] = vs[vsrc[d]];
         }
+        const float aa = hs[dA[0]], ab = hs[dA[2]], bA = hs[dA[1]];
+        const float ba = hs[dB[0]], bb = hs[dB[1]], bab = hs[dB[2]];
+        wave_sync_lds();   // every lane has read before the next round's stores
+        rot_cs(aa, bA, ab, cA, sA);
+        rot_cs(ba, bb, bab, cB, sB);
       }
     }
     // eigenvalues on the diagonal, eigenvectors in the columns (slot order)
@@ -1219,7 +1238,7 @@ struct Merge {
     // p <= 16: the one-wavefront Jacobi, whose 16 slots are ranked below
     int pr = p;
     if constexpr (P16 == 16) {
-      if (g.wave == 0) jacobi16(g, p, H, V);
+      if (g.wave == 0) jacobi16(g, p, H, V, Hn, Vn);
       __syncthreads();
       pr = 16;
     } else {
