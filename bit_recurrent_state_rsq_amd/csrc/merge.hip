@@ -41,12 +41,13 @@
 
 namespace rsq {
 
-// Subspace iterations: each one shrinks the error of the rank-k subspace by
-// about (sigma_(p+1) / sigma_k)^2, so a narrow bypass (few columns per kept
-// rank) needs more of them. With the warm start these bring the Frobenius
-// error within 1e-4 of the Eckart-Young optimum on the workloads' residuals.
-constexpr int kMergeItersWide = 5;    // p >= 4k + 4
-constexpr int kMergeItersMid = 6;     // p >= 3k + 4
+// Subspace iterations (products with C = R^T R): each one shrinks the error
+// of the rank-k subspace by about (sigma_(p+1) / sigma_k)^2, so a narrow
+// bypass (few columns per kept rank) needs more of them. With the warm start
+// these bring the Frobenius error within 2e-4 of the Eckart-Young optimum on
+// the workloads' residuals.
+constexpr int kMergeItersWide = 4;    // p >= 8k + 8
+constexpr int kMergeItersMid = 5;     // p >= 3k + 4
 constexpr int kMergeItersNarrow = 12;
 constexpr int kJacobiSweeps = 12;  // upper bound; stops once the off-diagonal part is negligible
 constexpr int kSm = kMaxCap + 1;   // row stride of the small p x p matrices
@@ -167,11 +168,29 @@ __device__ __forceinline__ float col_lane_sum(float v) {
 
 __device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// sum or max over the 64 lanes, the same value in every lane: within each
+// 16-lane row by DPP (quad permutes xor 1 and xor 2, half-row mirror, row
+// mirror), then rows 0 and 2 into rows 1 and 3 (row_bcast15) and lane 31 into
+// rows 2 and 3 (row_bcast31); lane 63 holds the total. No LDS round trip.
+template <int CTRL, int ROWS, bool SUM>
+__device__ __forceinline__ float dpp_step(float v) {
+  const int idn = __float_as_int(SUM ? 0.f : -INFINITY);   // rows left out keep the operation's identity
+  const float x = __int_as_float(__builtin_amdgcn_update_dpp(idn, __float_as_int(v), CTRL, ROWS, 0xF, false));
+  return SUM ? __fadd_rn(v, x) : fmaxf(v, x);
 }
+
+template <bool SUM>
+__device__ __forceinline__ float wave_reduce(float v) {
+  v = dpp_step<0xB1, 0xF, SUM>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_step<0x4E, 0xF, SUM>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_step<0x141, 0xF, SUM>(v);   // row_half_mirror
+  v = dpp_step<0x140, 0xF, SUM>(v);   // row_mirror
+  v = dpp_step<0x142, 0xA, SUM>(v);   // row_bcast15 into rows 1 and 3
+  v = dpp_step<0x143, 0xC, SUM>(v);   // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<true>(v); }
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -421,11 +440,7 @@ struct Merge {
   }
 
   // ------------------------------------------------------------ the factorisation on the matrix cores
-  static __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-  }
+  static __device__ __forceinline__ float wave_max(float v) { return wave_reduce<false>(v); }
 
   // e with m 2^e in [2^14, 2^15) for a finite m > 0 (binary16's largest finite is 65504)
   static __device__ __forceinline__ int fit_exp(float m) {
@@ -680,9 +695,10 @@ struct Merge {
   // One CholeskyQR pass src -> dst (N x p bases, column-major, N + 4 floats
   // per column; dst's columns from p to pc become zero), to be followed by a
   // barrier of the caller. Wavefront 0 forms the p x p Gram matrix of src 2^e
-  // on the matrix cores (split binary16, e from src's largest magnitude),
+  // on the matrix cores (split binary16, e from smax, a bound on src's magnitudes),
   // factors it (lane i holds row i; columns reach the other lanes by readlane)
-  // and inverts the factor (lane c forms column c of L^-1); after a barrier
+  // and inverts the factor (lane c forms column c of L^-1, reading L's rows by
+  // readlane); after a barrier
   // every thread applies dst = 2^e src L^-T to its rows. A column whose
   // remaining norm is below 1e-3 of its own (pivot below 1e-6 of its Gram
   // diagonal) gets a zero row in L^-1 and drops out. Returns, in every thread,
@@ -691,16 +707,15 @@ struct Merge {
   // rounded up to a supported unrolled size.
   template <int P16, int P8>
   static __device__ __forceinline__ float orth_pass(const Geo& g, const MergeLayout& ML, const float* src, float* dst,
-                                                    int p, float* ws, float* misc) {
+                                                    int p, float* ws, float* misc, float smax) {
     constexpr int NC = P16 / 16;
     const int N = ML.N;
     const size_t bs = (size_t)N + 4;
     const int l = g.lane;
-    float* Lr = ws;                          // rows of L (and first the Gram matrix)
-    float* dinv = ws + kMaxCap * kWs;        // 1/L_ii (0 for a dropped column)
+    float* Lr = ws;                          // the Gram matrix
     float* Mi = ws + (kMaxCap + 1) * kWs;    // rows of L^-1
     if (g.wave == 0) {
-      const int e = fit_exp(basis_max<NC>(g, src, N, p));
+      const int e = fit_exp(smax);
       // Gram blocks (a, b), a <= b: register r of lane l holds G[a*16 + 4(l/16) + r][b*16 + l%16]
       f4v G[NC][NC];
 #pragma unroll
@@ -755,31 +770,22 @@ struct Merge {
           row[j] = __builtin_fmaf(-lik, ljk, row[j]);
         }
       }
-      wave_sync_lds();   // every lane has read its Gram row
-      if (l < P8) {
-#pragma unroll
-        for (int c = 0; c < P8; c += 4)
-          *reinterpret_cast<f4v*>(Lr + l * kWs + c) = f4v{row[c], row[c + 1], row[c + 2], row[c + 3]};
-        dinv[l] = dmine;
-      }
-      wave_sync_lds();
-      // column l of L^-1: x_i = (i == l ? 1 : -sum_{t<i} L_it x_t) / L_ii, zero above l
-      if (l < P8) {
+      // L^-1: lane l forms column l, x_i = (i == l ? 1 : -sum_{t<i} L_it x_t) / L_ii
+      // (zero above l), taking row i of L (lane i's `row`) and 1/L_ii by readlane
+      if (true) {
         float x[P8];
 #pragma unroll
         for (int i = 0; i < P8; ++i) {
           float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int t4 = 0; t4 < i; t4 += 4) {
-            const f4v L4 = *reinterpret_cast<const f4v*>(Lr + i * kWs + t4);
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              if (t4 + t < i) s4[t] = __builtin_fmaf(L4[t], x[t4 + t], s4[t]);
+          for (int t = 0; t < i; ++t) {
+            const float lit = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row[t]), i));
+            s4[t & 3] = __builtin_fmaf(lit, x[t], s4[t & 3]);
           }
           const float su = __fadd_rn(__fadd_rn(s4[0], s4[1]), __fadd_rn(s4[2], s4[3]));
-          const float di = dinv[i];
+          const float di = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dmine), i));
           x[i] = (i == l) ? di : ((i < l) ? 0.f : -__fmul_rn(di, su));
-          Mi[i * kWs + l] = x[i];
+          if (l < P8) Mi[i * kWs + l] = x[i];
         }
       }
       // condition estimate: the live diagonal entries of L are the 1/dinv
@@ -1182,7 +1188,7 @@ struct Merge {
     if (g.lane == 0) misc[kMiscWave + g.wave] = fm;
     __syncthreads();
     for (int w = 0; w < g.nw; ++w) fm = fmaxf(fm, misc[kMiscWave + w]);
-    const int iters = (p >= 4 * k + 4) ? kMergeItersWide : (p >= 3 * k + 4) ? kMergeItersMid : kMergeItersNarrow;
+    const int iters = (p >= 8 * k + 8) ? kMergeItersWide : (p >= 3 * k + 4) ? kMergeItersMid : kMergeItersNarrow;
     float kappa = 1.f;
     // (the non-finite flags' slots: read long before, many barriers back)
     float* wmax = misc + kMiscWave + 8;
@@ -1192,9 +1198,10 @@ struct Merge {
       __syncthreads();
       ++it;
       // a well-conditioned basis takes a second product before it is
-      // orthonormalised again: the condition number grows by at most the
+      // orthonormalised again (never the last one, so that the final basis
+      // stays well conditioned): the condition number grows by at most the
       // product's, about the last estimate (uniform: every thread read it)
-      if (it < iters && kappa <= 4.f) {
+      if (it + 1 < iters && kappa <= 8.f) {
         float ym = 0.f;
         for (int w = 0; w < g.nw; ++w) ym = fmaxf(ym, wmax[w]);
         __syncthreads();   // the maxima are read before the next product rewrites them
@@ -1206,7 +1213,10 @@ struct Merge {
         Qb = Yb;
         Yb = t;
       }
-      kappa = orth_pass<P16, P8>(g, ML, Yb, Qb, p, wsc, misc);
+      // the product's largest magnitude (its wavefronts' maxima, out before the barrier)
+      float ym = 0.f;
+      for (int w = 0; w < g.nw; ++w) ym = fmaxf(ym, wmax[w]);
+      kappa = orth_pass<P16, P8>(g, ML, Yb, Qb, p, wsc, misc, ym);
       __syncthreads();
     }
     // CholeskyQR's loss of orthogonality grows like the square of the
@@ -1215,7 +1225,7 @@ struct Merge {
     // less than its tolerance; above, a second pass (CholeskyQR2). Uniform:
     // every thread read the same estimate.
     if (!(kappa <= 20.f)) {
-      orth_pass<P16, P8>(g, ML, Qb, Yb, p, wsc, misc);
+      orth_pass<P16, P8>(g, ML, Qb, Yb, p, wsc, misc, 1.f);   // unit columns: entries below 1
       __syncthreads();
       float* t = Qb;
       Qb = Yb;
