@@ -431,7 +431,8 @@ def quality_report(torch, rsq, w, hb, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--steps", type=int, default=500,
+                    help="timed steps (with a bypass: raised to a whole number of merge periods over all state sets)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps before timing (default: 4 per rotated state set, at least 16)")
     ap.add_argument("--age", type=int, default=32,
@@ -495,7 +496,14 @@ def main():
     nsets_guess = 1 if args.warm else int(np.ceil(args.min_set_bytes / rsq.state_bytes(**kw)))
     if args.warmup is None:
         args.warmup = max(16, 4 * nsets_guess)
+    if w.lrb_m:
+        # a whole number of merge periods over every state set, so that the
+        # wall clock holds exactly one merge per m steps of each set
+        period = nsets_guess * w.lrb_m
+        K = -(-K // period) * period
     q = time_steps(torch, rsq, w, kw, dev, K, args.warmup, args.age, args.warm, args.min_set_bytes, out)
+    if w.lrb_m and q["merges"] != K // w.lrb_m:
+        raise RuntimeError("timed region holds %d merges, not one per %d steps" % (q["merges"], w.lrb_m))
 
     bytes_step = rsq.workload_step_bytes(w.model, w.batch, hb, w.group, w.scale_dtype, w.d_k, w.d_v,
                                          w.in_dtype, w.lrb_k, w.lrb_m, w.pw_window)

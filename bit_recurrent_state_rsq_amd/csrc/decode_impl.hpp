@@ -534,14 +534,33 @@ struct Decode {
   // fp32 tile); kap: k_i s_i / F when `fast` (exact products), unused otherwise.
   // The gates and the lane's v values after the tree (`pre`, from dw_prefetch)
   // are loaded at the start of the step with the state, not here.
+  // INT4+Had with bf16 inputs known at compile time: q and the lane's 8 v
+  // values stay as their raw bf16 words (4 registers each instead of 8) until
+  // they are used, which keeps the rotated step within 128 registers
+  static constexpr bool kRawIn = kHad && SPEC != kSpecGeneric && SPEC != kSpecDynF32F32;
   struct DwPre {
-    float al, be, v[kHad ? 8 : NSLOT];   // the rotation needs v of the lane's own 8 columns
+    float al, be, v[kHad ? (kRawIn ? 1 : 8) : NSLOT];   // the rotation needs v of the lane's own 8 columns
+    uint32_t vr[kRawIn ? 4 : 1];
   };
+  // bf16 pair p of four raw words as two floats, converted where they are
+  // used: the empty asm keeps the conversion from being hoisted to the load
+  static __device__ __forceinline__ void raw_bf16x8(const uint32_t r[4], float out[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t w = r[p];
+      asm volatile("" : "+v"(w));
+      out[2 * p] = __uint_as_float(w << 16);
+      out[2 * p + 1] = __uint_as_float(w & 0xFFFF0000u);
+    }
+  }
   static __device__ __forceinline__ DwPre dw_prefetch(const StepArgs& a, int tile, int j0, int lane) {
     DwPre p;
     p.al = a.alpha[tile];
     p.be = a.beta[tile];
-    if constexpr (kHad) {
+    if constexpr (kRawIn) {
+      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.v) + (size_t)tile * a.dv + j0);
+      p.vr[0] = u.x, p.vr[1] = u.y, p.vr[2] = u.z, p.vr[3] = u.w;
+    } else if constexpr (kHad) {
       load8(SP::bf16(a), a.v, (size_t)tile * a.dv + j0, p.v);
     } else {
 #pragma unroll
@@ -611,10 +630,16 @@ struct Decode {
       const int gl = SP::GL > 0 ? SP::GL : (a.group >> 3);
       const float ig = 1.0f / (float)(8 * gl);   // 1/g, a power of two
       fwht8(wv, gl, lane);
+      float v8l[8];
+      if constexpr (kRawIn) raw_bf16x8(pre.vr, v8l);
+      else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v8l[j] = pre.v[j];
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float u = __fmul_rn(wv[j], ig);
-        wv[j] = __fmul_rn(be, __fsub_rn(pre.v[j], __fmul_rn(al, u)));
+        wv[j] = __fmul_rn(be, __fsub_rn(v8l[j], __fmul_rn(al, u)));
       }
       fwht8(wv, gl, lane);
     }
@@ -699,8 +724,14 @@ struct Decode {
       pw_ub = *reinterpret_cast<const uint2*>(tb + he.bypass_u + (size_t)slot * a.dk + i0);
       pw_wb = *reinterpret_cast<const uint2*>(tb + he.bypass_w + (size_t)slot * a.dv + j0);
     }
-    float qf[8], kf[8], dec[8];
-    load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
+    float qf[kRawIn ? 1 : 8], kf[8], dec[8];
+    uint32_t qr[kRawIn ? 4 : 1];
+    if constexpr (kRawIn) {
+      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) + (size_t)tile * a.dk + i0);
+      qr[0] = u.x, qr[1] = u.y, qr[2] = u.z, qr[3] = u.w;
+    } else {
+      load8(bf16, a.q, (size_t)tile * a.dk + i0, qf);
+    }
     load8(bf16, a.k, (size_t)tile * a.dk + i0, kf);
     decays(a, he, tile, i0, dec);
     DwPre dwp{};
@@ -821,12 +852,17 @@ struct Decode {
 
     // readout partial o_j over this wavefront's rows
     {
-      float o8[8];
+      float o8[8], q8[8];
+      if constexpr (kRawIn) raw_bf16x8(qr, q8);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q8[i] = qf[i];
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float acc = __fmul_rn(qf[0], x[0][j]);
+        float acc = __fmul_rn(q8[0], x[0][j]);
 #pragma unroll
-        for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(qf[i], x[i][j], acc);
+        for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(q8[i], x[i][j], acc);
         o8[j] = acc;
       }
       xtree<NB>(o8, lane);

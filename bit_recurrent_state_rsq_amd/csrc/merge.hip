@@ -24,16 +24,24 @@
 // split into a high and a low binary16 part, and the three products hi*hi,
 // hi*lo and lo*hi accumulate in float32 (the dropped lo*lo term is below
 // 2^-22 of each product). A fixed number of subspace iterations
-//   Q <- orth(C Q)
-// start from the bypass's own factors on that side (which span the row or
-// column space of L), with C Q again on split binary16 matrix cores. orth is
-// CholeskyQR (CholeskyQR2 for the last basis), which every wavefront computes
-// for itself so that no barrier separates the Gram matrix, its Cholesky
-// factor and the triangular solve. Rayleigh-Ritz then diagonalises the p x p
-// matrix Q^T C Q by cyclic Jacobi; its top k eigenpairs (sigma^2, v) give the
-// narrow-side singular vectors Q v, and the other side's R (Q v) / sigma
-// comes from R, which every lane still holds in registers in the decode
-// kernel's 8x8-chunk layout.
+//   Q <- orth(C Q)   (or orth(C C Q) while the basis stays well conditioned)
+// start from the bypass's own factors on that side, which span the row or
+// column space of L (an all-zero start column gets a fixed +-1 pattern), with
+// C Q again on split binary16 matrix cores. orth is CholeskyQR: wavefront 0
+// forms the basis's Gram matrix on the matrix cores, factors it and inverts
+// the factor with cross-lane reads, and every thread then applies the inverse
+// to its rows; a second pass (CholeskyQR2) follows when the first one's
+// condition estimate is above 20. Rayleigh-Ritz then diagonalises the p x p
+// matrix Q^T C Q by cyclic Jacobi (in one wavefront when p <= 16); its top k
+// eigenpairs (sigma^2, v) give the narrow-side singular vectors Q v, and the
+// other side's R (Q v) / sigma comes from R, which every lane still holds in
+// registers in the decode kernel's 8x8-chunk layout.
+//
+// Working on C squares R's condition number. A direction of R whose singular
+// value is below a few percent of the largest sinks, in C Q, below the
+// CholeskyQR pivot threshold and can be lost; that costs accuracy only when
+// fewer than k directions are stronger, so that the kept rank reaches down to
+// such a weak one.
 #include <algorithm>
 
 #include "rsq_kernels.hpp"
@@ -238,14 +246,28 @@ struct Merge {
   }
 
   // ------------------------------------------------------------ merge into the codes
-  // U and W (binary16) of the tile into LDS, column-major like in memory
+  // U and W (binary16) of the tile into LDS, column-major like in memory (W
+  // right after U): every thread issues up to two 16-byte loads before it
+  // stores any of them
   static __device__ __forceinline__ void stage_bypass(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
-                                                      __half* us, __half* ws) {
+                                                      __half* us) {
     const uint4* U = reinterpret_cast<const uint4*>(tb + he.bypass_u);
     const uint4* W = reinterpret_cast<const uint4*>(tb + he.bypass_w);
-    const int nu = a.n * a.dk / 8, nwv = a.n * a.dv / 8;   // 16-byte pieces
-    for (int e = threadIdx.x; e < nu; e += blockDim.x) reinterpret_cast<uint4*>(us)[e] = U[e];
-    for (int e = threadIdx.x; e < nwv; e += blockDim.x) reinterpret_cast<uint4*>(ws)[e] = W[e];
+    const int nu = a.n * a.dk / 8, tot = nu + a.n * a.dv / 8;   // 16-byte pieces
+    uint4* dst = reinterpret_cast<uint4*>(us);
+    const int nt = blockDim.x;
+    for (int e = threadIdx.x; e < tot; e += 2 * nt) {
+      const int e2 = e + nt;
+      // (no branch between the loads and the stores: a thread without a
+      // second piece loads and stores its first one twice)
+      const bool two = e2 < tot;
+      const int f = two ? e2 : e;
+      const uint4* p0 = (e < nu) ? U + e : W + (e - nu);
+      const uint4* p1 = (f < nu) ? U + f : W + (f - nu);
+      const uint4 v0 = *p0, v1 = *p1;
+      dst[e] = v0;
+      dst[f] = v1;
+    }
     __syncthreads();
   }
 
@@ -271,9 +293,11 @@ struct Merge {
   // Moves the elements of L above the threshold into the codes and
   // requantizes the chunk. Leaves in mk[i] the moved elements of row i:
   // bit j when L_ij > 0, bit 8+j when L_ij < 0.
+  // The lane's codes and step sizes are loaded before the bypass factors are
+  // staged, so that both reads share one round trip to memory.
   template <int BITS>
   static __device__ __forceinline__ void requantize(const StepArgs& a, const HeadEntry& he, uint8_t* tb, const Geo& g,
-                                                    const __half* us, const __half* ws, uint32_t mk[8],
+                                                    __half* us, __half* ws, uint32_t mk[8],
                                                     float L[8][8], uint32_t& flags) {
     const bool sf16 = a.scale_f16 != 0;
     const int G = g.j0 / a.group;
@@ -282,8 +306,20 @@ struct Merge {
     uint8_t* sp = tb + he.scales + ((size_t)G * a.dk + g.i0) * (sf16 ? 2 : 4);
     Chunk<BITS> ch;
     load_chunk<BITS>(cp, ch);
+    // the step sizes' raw words: converted after the staging, so that no wait
+    // for them comes before its loads
+    uint4 sraw[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
+    sraw[0] = *reinterpret_cast<const uint4*>(sp);
+    if (!sf16) sraw[1] = *reinterpret_cast<const uint4*>(sp + 16);
+    stage_bypass(a, he, tb, us);
     float s_old[8];
-    load_scales8(sf16, sp, s_old);
+    {
+      const uint32_t w[8] = {sraw[0].x, sraw[0].y, sraw[0].z, sraw[0].w, sraw[1].x, sraw[1].y, sraw[1].z, sraw[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        s_old[i] = sf16 ? __half2float(__ushort_as_half((uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu))))
+                        : __uint_as_float(w[i]);
+    }
     // the codes are unpacked row by row where needed (unused rows of an
     // inlined unpack are dropped), which keeps the live set to L or x plus q
     float x[8][8];
@@ -1353,7 +1389,6 @@ struct Merge {
     // the bypass factors go through LDS; L is formed once from them and kept for R
     __half* us = reinterpret_cast<__half*>(lds);
     __half* wst = us + (size_t)a.n * a.dk;
-    stage_bypass(a, he, tb, us, wst);
     uint32_t mk[8];
     float R[8][8];   // L, kept through the requantization
     switch (he.bits) {
