@@ -255,35 +255,79 @@ struct Spec {
 typedef __attribute__((address_space(1))) uint32_t g_u32;
 typedef __attribute__((address_space(1))) uint16_t g_u16;
 typedef __attribute__((address_space(1))) uint8_t g_u8;
-template <bool BF16>
-static __device__ __forceinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, const void* qp, int tile, int dk, int W,
+// The words the pairs' phase reads, loaded in one batch before the state's
+// stores (the loads then do not wait behind them on the in-order memory
+// counter): lane l's key bytes of the pairs c = wave + nw m, and k, q of its
+// rows (raw: a bf16 input's 16 bits, shifted into a float where used, so that
+// no wait for them comes before the stores). Also, for the new pair and the
+// readout's window term:
+// k of row tid and v of column tid mod d_v, and the window's E4M3 w bytes of
+// the readout's columns c = tid / d_v + m (block / d_v) (clamped indices: every
+// load is unconditional).
+struct PwPre {
+  uint32_t pre[4], kb[4], qb[4];
+  uint32_t kn, vn;
+  uint32_t wb[4];
+  float al, be;   // the step's gates, as the state's step loaded them
+  __device__ __forceinline__ static float f(uint32_t raw, bool bf16) { return __uint_as_float(bf16 ? raw << 16 : raw); }
+};
+static __device__ __forceinline__ void pw_prefetch(const uint8_t* U8, const uint8_t* W8, const void* kp, const void* qp,
+                                                   const void* vp, bool bf16, int tile, int dk, int dv, int W,
+                                                   PwPre& p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int R = dk >= 64 ? dk >> 6 : 1;
+  const int i0 = lane * R;
+  const g_u32* U = (const g_u32*)reinterpret_cast<const uint32_t*>(U8);
+  const int wi = min(i0, dk - 1) >> 2;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) p.pre[m] = U[(size_t)min(wave + nw * m, W - 1) * (dk >> 2) + wi];
+  const int t = threadIdx.x, P = (int)blockDim.x / dv, j = t % dv, pp = t / dv;
+  const size_t ik = (size_t)tile * dk + min(t, dk - 1), iv = (size_t)tile * dv + j;
+  if (bf16) {
+    const g_u16* K16 = (const g_u16*)reinterpret_cast<const uint16_t*>(kp);
+    const g_u16* Q16 = (const g_u16*)reinterpret_cast<const uint16_t*>(qp);
+    const g_u16* V16 = (const g_u16*)reinterpret_cast<const uint16_t*>(vp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t idx = (size_t)tile * dk + min(i0 + e, dk - 1);
+      p.kb[e] = K16[idx];
+      p.qb[e] = Q16[idx];
+    }
+    p.kn = K16[ik];
+    p.vn = V16[iv];
+  } else {
+    const g_u32* K32 = (const g_u32*)reinterpret_cast<const uint32_t*>(kp);
+    const g_u32* Q32 = (const g_u32*)reinterpret_cast<const uint32_t*>(qp);
+    const g_u32* V32 = (const g_u32*)reinterpret_cast<const uint32_t*>(vp);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t idx = (size_t)tile * dk + min(i0 + e, dk - 1);
+      p.kb[e] = K32[idx];
+      p.qb[e] = Q32[idx];
+    }
+    p.kn = K32[ik];
+    p.vn = V32[iv];
+  }
+  const g_u8* Wb = (const g_u8*)W8;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) p.wb[m] = Wb[(size_t)min(pp + m * max(P, 1), W - 1) * dv + j];
+}
+
+// R = d_k / 64 rows per lane (d_k a power of two, 64 .. 256), or one row
+// (d_k < 64, lanes past d_k adding zeros)
+template <int R>
+static __device__ __forceinline__ void pw_pairs_r4(uint8_t* U8, const PwPre& pf, bool bf16, int dk, int W,
                                               int n, int slot, float al, float be, float* z) {
   const bool leaving = n == W;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const int R = dk >= 64 ? dk >> 6 : 1;   // 1, 2 or 4
   const int i0 = lane * R;                 // the lane's first row
   const bool rows_ok = i0 < dk;
-  g_u32* U = (g_u32*)reinterpret_cast<uint32_t*>(U8);
-  const g_u16* K16 = (const g_u16*)reinterpret_cast<const uint16_t*>(kp);
-  const g_u16* Q16 = (const g_u16*)reinterpret_cast<const uint16_t*>(qp);
-  const g_u32* K32 = (const g_u32*)reinterpret_cast<const uint32_t*>(kp);
-  const g_u32* Q32 = (const g_u32*)reinterpret_cast<const uint32_t*>(qp);
-  uint32_t pre[4], kb[4], qb[4];
-  const int wi = min(i0, dk - 1) >> 2, sh = 8 * (i0 & 3);
+  const int sh = 8 * (i0 & 3);
+  float k4[R], q4[R];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) pre[m] = U[(size_t)min(wave + nw * m, W - 1) * (dk >> 2) + wi];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const size_t idx = (size_t)tile * dk + min(i0 + e, dk - 1);
-    kb[e] = BF16 ? (uint32_t)K16[idx] << 16 : K32[idx];
-    qb[e] = BF16 ? (uint32_t)Q16[idx] << 16 : Q32[idx];
-  }
-  float k4[4], q4[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool ok = e < R && rows_ok;
-    k4[e] = ok ? __uint_as_float(kb[e]) : 0.f;
-    q4[e] = ok ? __uint_as_float(qb[e]) : 0.f;
+  for (int e = 0; e < R; ++e) {
+    k4[e] = rows_ok ? PwPre::f(pf.kb[e], bf16) : 0.f;
+    q4[e] = rows_ok ? PwPre::f(pf.qb[e], bf16) : 0.f;
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -295,17 +339,19 @@ static __device__ __forceinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, 
     float zacc = 0.f;
     if (is_new) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(k4[e])), q4[e], zacc);
+      for (int e = 0; e < R; ++e) zacc = __builtin_fmaf(e4m3_to_f32(f32_to_e4m3(k4[e])), q4[e], zacc);
     } else {
-      const uint32_t ub = pre[m] >> sh;
-      float ue[4], pe[4];
+      const uint32_t ub = pf.pre[m] >> sh;
+      float ue[R], pe[R];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ue[e] = (e < R && rows_ok) ? e4m3_to_f32((ub >> (8 * e)) & 0xFFu) : 0.f;
+      for (int e = 0; e < R; ++e) {
+        const float u = e == 0 ? e4m3_byte_to_f32<0>(ub) : e == 1 ? e4m3_byte_to_f32<1>(ub)
+                      : e == 2 ? e4m3_byte_to_f32<2>(ub) : e4m3_byte_to_f32<3>(ub);
+        ue[e] = rows_ok ? u : 0.f;
         pe[e] = __fmul_rn(k4[e], ue[e]);
       }
-      if (1 < R) { pe[0] = __fadd_rn(pe[0], pe[1]); pe[2] = __fadd_rn(pe[2], pe[3]); }
-      if (2 < R) pe[0] = __fadd_rn(pe[0], pe[2]);
+      if constexpr (R == 2) pe[0] = __fadd_rn(pe[0], pe[1]);
+      if constexpr (R == 4) pe[0] = __fadd_rn(__fadd_rn(pe[0], pe[1]), __fadd_rn(pe[2], pe[3]));
       float d = pe[0];
       d = __fadd_rn(d, dpp_xor1(d));
       d = __fadd_rn(d, dpp_xor2(d));
@@ -314,19 +360,23 @@ static __device__ __forceinline__ void pw_pairs_r4(uint8_t* U8, const void* kp, 
       d = __fadd_rn(d, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(d), 0x401F)));
       d = __fadd_rn(d, __shfl_xor(d, 32, 64));
       const float b = __fmul_rn(be, d);
-      uint32_t codes = 0;
+      float nv[R];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t code = f32_to_e4m3(__fmul_rn(al, __fsub_rn(ue[e], __fmul_rn(b, k4[e]))));
-        if (e < R) {
-          codes |= code << (8 * e);
-          zacc = __builtin_fmaf(e4m3_to_f32(code), q4[e], zacc);
-        }
+      for (int e = 0; e < R; ++e) nv[e] = __fmul_rn(al, __fsub_rn(ue[e], __fmul_rn(b, k4[e])));
+      uint32_t codes;
+      if constexpr (R == 1) codes = f32_to_e4m3(nv[0]);
+      else if constexpr (R == 2) codes = f32x2_to_e4m3(nv[0], nv[1]);
+      else codes = f32x2_to_e4m3(nv[0], nv[1]) | (f32x2_to_e4m3(nv[2], nv[3]) << 16);
+#pragma unroll
+      for (int e = 0; e < R; ++e) {
+        const float u = e == 0 ? e4m3_byte_to_f32<0>(codes) : e == 1 ? e4m3_byte_to_f32<1>(codes)
+                      : e == 2 ? e4m3_byte_to_f32<2>(codes) : e4m3_byte_to_f32<3>(codes);
+        zacc = __builtin_fmaf(u, q4[e], zacc);
       }
       if (rows_ok) {
         g_u8* dst = (g_u8*)(U8 + (size_t)c * dk + i0);
-        if (R == 4) *(g_u32*)dst = codes;
-        else if (R == 2) *(g_u16*)dst = (uint16_t)codes;
+        if constexpr (R == 4) *(g_u32*)dst = codes;
+        else if constexpr (R == 2) *(g_u16*)dst = (uint16_t)codes;
         else *dst = (uint8_t)codes;
       }
     }
@@ -684,7 +734,7 @@ struct Decode {
   template <int BITS, bool BOOST = false>
   static __device__ __forceinline__ void body(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                               const Lds& L, uint32_t& flags, const BypassRegs* br = nullptr,
-                                              bool byp_regs = false) {
+                                              bool byp_regs = false, PwPre* pwp = nullptr) {
     const bool bf16 = SP::bf16(a), sf16 = SP::sf16(a);
     const int smode = SP::smode(a);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -816,13 +866,10 @@ struct Decode {
     if constexpr (kPW) {
       if (pw_leaving) {
         float ue[8], we[8], t8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ue[e] = e4m3_to_f32((pw_ub.x >> (8 * e)) & 0xFFu);
-          ue[e + 4] = e4m3_to_f32((pw_ub.y >> (8 * e)) & 0xFFu);
-          we[e] = e4m3_to_f32((pw_wb.x >> (8 * e)) & 0xFFu);
-          we[e + 4] = e4m3_to_f32((pw_wb.y >> (8 * e)) & 0xFFu);
-        }
+        e4m3_bytes4(pw_ub.x, ue);
+        e4m3_bytes4(pw_ub.y, ue + 4);
+        e4m3_bytes4(pw_wb.x, we);
+        e4m3_bytes4(pw_wb.y, we + 4);
 #pragma unroll
         for (int i = 0; i < 8; ++i) t8[i] = __fmul_rn(kf[i], ue[i]);
         float d = row_lane_sum<NB>(tree8(t8));
@@ -1181,6 +1228,14 @@ struct Decode {
         diagnostics<BITS>(a, tile, i0, j0, t, xk, r, s_new, inv, kf, wv, dec);
       Chunk<BITS> out;
       pack_t(t, out);
+      // the window's reads go out before the state's stores
+      if constexpr (kPW) {
+        if (pw_fits_r4(a)) {
+          pw_prefetch(tb + he.bypass_u, tb + he.bypass_w, a.k, a.q, a.v, bf16, tile, a.dk, a.dv, a.pw, *pwp);
+          pwp->al = dwp.al;
+          pwp->be = dwp.be;
+        }
+      }
       store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
       if constexpr (kSplit8) {
@@ -1285,12 +1340,25 @@ struct Decode {
   // Pure-write window: the pairs' transitions and the readout projections
   // (pw_pairs below), kept out of line so that its registers do not add to
   // the body's.
+  // The pairs' phase reads its words from the batch loaded before the
+  // state's stores when d_k <= 256 and every wavefront has at most 4 pairs.
+  static __device__ __forceinline__ bool pw_fits_r4(const StepArgs& a) {
+    return a.dk <= 256 && a.pw <= 4 * (int)(blockDim.x >> 6);
+  }
+  // ... and the new pair and the readout's window term too when every thread
+  // has at most one row of k, one column of v and four window columns
+  static __device__ __forceinline__ bool pw_fits_all(const StepArgs& a) {
+    const int nt = blockDim.x;
+    return pw_fits_r4(a) && a.dk <= nt && a.dv <= nt && a.pw <= 4 * (nt / a.dv);
+  }
   static __device__ __forceinline__ void pw_phase(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                                  float* z) {
+                                                  float* z, const PwPre& pf) {
     const int slot = (int)((a.t_next - 1) % a.pw);
-    if (a.dk <= 256 && a.pw <= 4 * (int)(blockDim.x >> 6)) {
-      if (SP::bf16(a)) pw_pairs_r4<true>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
-      else pw_pairs_r4<false>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
+    if (pw_fits_r4(a)) {
+      const int R = a.dk >= 64 ? a.dk >> 6 : 1;
+      if (R == 1) pw_pairs_r4<1>(tb + he.bypass_u, pf, SP::bf16(a), a.dk, a.pw, a.n, slot, pf.al, pf.be, z);
+      else if (R == 2) pw_pairs_r4<2>(tb + he.bypass_u, pf, SP::bf16(a), a.dk, a.pw, a.n, slot, pf.al, pf.be, z);
+      else pw_pairs_r4<4>(tb + he.bypass_u, pf, SP::bf16(a), a.dk, a.pw, a.n, slot, pf.al, pf.be, z);
       return;
     }
     if (SP::bf16(a)) pw_pairs<true>(tb + he.bypass_u, a.k, a.q, tile, a.dk, a.pw, a.n, slot, a.alpha[tile], a.beta[tile], z);
@@ -1299,12 +1367,18 @@ struct Decode {
 
   // The new pure write (e4m3(k_t), e4m3(fl(beta_t v_t))) into slot (t - 1) mod W.
   static __device__ __forceinline__ void pw_write_new_pair(const StepArgs& a, const HeadEntry& he, uint8_t* tb,
-                                                           int tile) {
+                                                           int tile, const PwPre& pf) {
     const int slot = (int)((a.t_next - 1) % a.pw);
     const bool bf16 = SP::bf16(a);
-    const float be = a.beta[tile];
     uint8_t* U = tb + he.bypass_u + (size_t)slot * a.dk;
     uint8_t* W = tb + he.bypass_w + (size_t)slot * a.dv;
+    if (pw_fits_all(a)) {
+      const int t = threadIdx.x;
+      if (t < a.dk) U[t] = (uint8_t)f32_to_e4m3(PwPre::f(pf.kn, bf16));
+      if (t < a.dv) W[t] = (uint8_t)f32_to_e4m3(__fmul_rn(pf.be, PwPre::f(pf.vn, bf16)));
+      return;
+    }
+    const float be = a.beta[tile];
     for (int i = threadIdx.x; i < a.dk; i += blockDim.x)
       U[i] = (uint8_t)f32_to_e4m3(in_elem(bf16, a.k, (size_t)tile * a.dk + i));
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x)
@@ -1350,13 +1424,14 @@ struct Decode {
       }
     }
 
+    PwPre pwp{};
     if constexpr (kF32) {
       body<32, BOOST>(a, he, tb, tile, L, flags);
     } else {
       switch (he.bits) {
-        case 4: body<4, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
-        case 6: body<6, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
-        default: body<8, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs); break;
+        case 4: body<4, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs, &pwp); break;
+        case 6: body<6, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs, &pwp); break;
+        default: body<8, BOOST>(a, he, tb, tile, L, flags, &br, byp_regs, &pwp); break;
       }
     }
     if constexpr (kBypass) {
@@ -1365,23 +1440,23 @@ struct Decode {
     // the staying window pairs: after the state's step, whose loads then go
     // out first (the pairs never touch the leaving pair's slot, which the
     // state's step reads)
-    if constexpr (kPW) pw_phase(a, he, tb, tile, L.z);
+    if constexpr (kPW) pw_phase(a, he, tb, tile, L.z, pwp);
     if constexpr (kPW) {
       // every wavefront has read the leaving pair: the new one takes its slot
       __syncthreads();
-      pw_write_new_pair(a, he, tb, tile);
+      pw_write_new_pair(a, he, tb, tile, pwp);
     }
     if (wrw > 1 || kBypass || kPW || kHad) {
       __syncthreads();
       // combine readout partials over row-wavefronts, add the bypass term, store o
-      combine_o(a, he, tb, tile, L, wrw, flags, byp_regs, br);
+      combine_o(a, he, tb, tile, L, wrw, flags, byp_regs, br, pwp);
     }
     finish(a, tile, flags);
   }
 
   static __device__ __forceinline__ void combine_o(const StepArgs& a, const HeadEntry& he, const uint8_t* tb,
                                                    int tile, const Lds& L, int wrw, uint32_t& flags,
-                                                   bool byp_regs, BypassRegs& br) {
+                                                   bool byp_regs, BypassRegs& br, const PwPre& pf) {
     // bypass columns (fp16) / window pairs (E4M3): cnt columns of W, each
     // weighted by its z. The sum W z is spread over every thread of the
     // block: thread (p, j) takes columns p, p + P, ... of row j of W (its
@@ -1405,7 +1480,17 @@ struct Decode {
           const float w_new = MODEL == kGDN ? L.w[(j / WC) * wrw * WC + j % WC] : 0.f;
           part = bypass_wz_part(a, MODEL, SP::bf16(a), br, L.z, w_new);
         }
-        else
+        else if (kPW && pw_fits_all(a)) {
+          // the window's w bytes from the early batch; the new pair's slot
+          // holds e4m3(beta v_j) now
+          const int slot = (int)((a.t_next - 1) % a.pw);
+          const float wnew = e4m3_to_f32(f32_to_e4m3(__fmul_rn(pf.be, PwPre::f(pf.vn, SP::bf16(a)))));
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int c = pp + m * P;
+            if (c < cnt) part = __builtin_fmaf(c == slot ? wnew : e4m3_to_f32(pf.wb[m]), L.z[c], part);
+          }
+        } else
           for (int c = pp; c < cnt; c += P) part = __builtin_fmaf(wval(c, j), L.z[c], part);
         L.up[pp * a.dv + j] = part;
       }

@@ -33,29 +33,42 @@ constexpr int kMaxCap = 32;   // bypass columns a kernel can hold
 
 // OCP E4M3 (exponent bias 7, 3 mantissa bits, largest finite 448, no
 // infinities): round to nearest-even, saturate to +-448, NaN -> 0x7F with the
-// sign kept. Below 2^-6 the grid is the multiples of 2^-9 (a * 512 is exact).
+// sign kept. gfx950's conversion instructions use this format: v_cvt_pk_fp8_f32
+// rounds to nearest-even, and with its input clamped to +-448 first it
+// saturates as above; v_cvt_f32_fp8 is exact. Checked against a bitwise
+// software encoder over all 2^32 float inputs and all 256 codes: the only
+// difference is the sign the encoder gives a NaN, which is set here.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  // branch-free: the subnormal and normal encodings are both formed and one
-  // is selected (below 2^-6 the code is RNE(|x| 512), codes 0 .. 8)
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(a, 1.f) * 512.f);
-  uint32_t r = __float_as_uint(a);
-  r = (r + 0x7FFFFu + ((r >> 20) & 1u)) & 0xFFF00000u;                    // RNE to 3 mantissa bits
-  const uint32_t e = (r >> 23) - 120u, m = (r >> 20) & 7u;                 // exponent field, bias 7
-  const uint32_t nor = (e > 15u || (e == 15u && m == 7u)) ? 0x7Eu : ((e << 3) | m);   // saturate to 448
-  uint32_t c = a < 0x1p-6f ? sub : nor;
-  c = (a == a) ? c : 0x7Fu;
-  return sign | c;
+  const float xc = fminf(fmaxf(x, -448.f), 448.f);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xc, xc, 0, false) & 0xFFu;
+  return (x == x) ? c : (0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u));
+}
+
+// two codes at once: a in bits 0-7, b in bits 8-15
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  const float ac = fminf(fmaxf(a, -448.f), 448.f), bc = fminf(fmaxf(b, -448.f), 448.f);
+  uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ac, bc, 0, false) & 0xFFFFu;
+  if (!(a == a)) c = (c & 0xFF00u) | 0x7Fu | ((__float_as_uint(a) >> 24) & 0x80u);
+  if (!(b == b)) c = (c & 0x00FFu) | ((0x7Fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+  return c;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float sub = (float)m * 0x1p-9f;
-  const float nor = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  float v = e == 0 ? sub : nor;
-  v = (c & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : v;
-  return __uint_as_float(__float_as_uint(v) | ((c & 0x80u) << 24));
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+
+// code SEL (byte SEL) of a packed word
+template <int SEL>
+__device__ __forceinline__ float e4m3_byte_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
+}
+
+// the four codes of a packed word, byte 0 first
+__device__ __forceinline__ void e4m3_bytes4(uint32_t w, float out[4]) {
+  out[0] = e4m3_byte_to_f32<0>(w);
+  out[1] = e4m3_byte_to_f32<1>(w);
+  out[2] = e4m3_byte_to_f32<2>(w);
+  out[3] = e4m3_byte_to_f32<3>(w);
 }
 
 // Round-to-nearest-even of an exact product through the float32 adder:
