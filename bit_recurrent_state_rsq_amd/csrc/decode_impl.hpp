@@ -912,9 +912,18 @@ struct Decode {
         for (int i = 1; i < 8; ++i) acc = __builtin_fmaf(q8[i], x[i][j], acc);
         o8[j] = acc;
       }
+      if constexpr (kHad) {
+        // the readout of the rotated state is o~ = S~^T q; o = o~ H / g. The
+        // rotation is linear, so it is applied to the lane's partial sums,
+        // before the sum over rows (the readout's order is free)
+        const float ig = 1.0f / (float)(8 * gl);   // 1/g, a power of two
+        fwht8(o8, gl, lane);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o8[j] = __fmul_rn(o8[j], ig);
+      }
       xtree<NB>(o8, lane);
       const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
-      if (wrw == 1 && !kBypass && !kPW && !kHad) {
+      if (wrw == 1 && !kBypass && !kPW) {
         // one wavefront covers every row: its sums are the readout
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
@@ -1446,7 +1455,7 @@ struct Decode {
       __syncthreads();
       pw_write_new_pair(a, he, tb, tile, pwp);
     }
-    if (wrw > 1 || kBypass || kPW || kHad) {
+    if (wrw > 1 || kBypass || kPW) {
       __syncthreads();
       // combine readout partials over row-wavefronts, add the bypass term, store o
       combine_o(a, he, tb, tile, L, wrw, flags, byp_regs, br, pwp);
@@ -1499,11 +1508,6 @@ struct Decode {
     for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
       float acc = L.op[j];
       for (int q = 1; q < wrw; ++q) acc += L.op[q * a.dv + j];
-      if constexpr (kHad) {
-        // the readout of the rotated state: o~, rotated back below
-        L.up[j] = acc;
-        continue;
-      }
       if (kWz) {
         if (P >= 1) {
           for (int pp = 0; pp < P; ++pp) acc += L.up[pp * a.dv + j];
@@ -1513,34 +1517,6 @@ struct Decode {
       }
       if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
       a.o[(size_t)tile * a.dv + j] = acc;
-    }
-    if constexpr (kHad) {
-      // o = o~ H / g, group by group (H_jj' = (-1)^popcount(j & j') inside a group)
-      __syncthreads();
-      const int g = a.group;
-      const float ig = 1.0f / (float)g;
-      for (int j = threadIdx.x; j < a.dv; j += blockDim.x) {
-        float acc;
-        if (g <= 64) {
-          // the butterflies of the fast transform, across the lanes of a
-          // group (groups are aligned, so a lane's partners are all live)
-          acc = L.up[j];
-          for (int m = 1; m < g; m <<= 1) {
-            const float o = __shfl_xor(acc, m, 64);
-            acc = (j & m) ? __fsub_rn(o, acc) : __fadd_rn(acc, o);
-          }
-        } else {
-          const int base = j & ~(g - 1), jj = j & (g - 1);
-          acc = 0.f;
-          for (int t = 0; t < g; ++t) {
-            const float v = L.up[base + t];
-            acc += (__builtin_popcount(t & jj) & 1) ? -v : v;
-          }
-        }
-        acc = __fmul_rn(acc, ig);
-        if (!(fabsf(acc) <= 3.4e38f)) flags |= kStatusNonfinite;
-        a.o[(size_t)tile * a.dv + j] = acc;
-      }
     }
   }
 
