@@ -530,6 +530,8 @@ struct Decode {
     float* z;      // [kMaxCap] + [nw][kMaxCap]  bypass readout projections
     float* zk;     // [kMaxCap]  delta rule with a bypass: z_c = U_c^T k
     float* bz;     // [dv]       delta rule with a bypass: b = W z
+    __half* wst;   // gdn_wstage_bytes(dv)  delta rule with a bypass: W's columns, staged
+    uint8_t* ust;  // gdn_ustage_bytes(dk)  ... and U's
   };
 
   static __device__ __forceinline__ void decays(const StepArgs& a, const HeadEntry& he, int tile, int i0,
@@ -837,7 +839,7 @@ struct Decode {
     if constexpr (MODEL == kGDN && kBypass) {
       // the bypass's share of the retrieval, b = W (U^T k), from the values
       // loaded at kernel start (the loop form ran before this step)
-      if (byp_regs && a.n > 0) gdn_bypass_retrieval_regs(a, SP::bf16(a), *br, L.zk, L.bz);
+      if (byp_regs && a.n > 0) gdn_bypass_retrieval_regs(a, SP::bf16(a), *br, L.zk, L.bz, L.wst, L.ust);
       __half* wn = reinterpret_cast<__half*>(tb + he.bypass_w) + (size_t)a.n * a.dv;
       delta_w<BITS>(a, tile, x, kf, smul, kap, fast, dwp, wv, L.w, L.up, wrw, wr, j0, lane, wave,
                     a.n > 0 ? L.bz : nullptr, wn);
@@ -1414,6 +1416,8 @@ struct Decode {
     L.z = L.op + wrw * a.dv;                  // [kMaxCap] + [nw][kMaxCap]
     L.zk = L.z + kMaxCap * (1 + nw);          // [kMaxCap]
     L.bz = L.zk + kMaxCap;                    // [dv]
+    L.wst = reinterpret_cast<__half*>(L.bz + a.dv);
+    L.ust = reinterpret_cast<uint8_t*>(L.wst) + gdn_wstage_bytes(a.dv);
     uint32_t flags = 0;
 
     // bypass: its loads join the state's (values held in registers) when
@@ -1423,7 +1427,7 @@ struct Decode {
     if constexpr (kBypass) {
       byp_regs = bypass_regs_fit(a, MODEL);
       if (byp_regs) {
-        bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br);
+        bypass_load(a, he, tb, tile, MODEL, SP::bf16(a), br, L.wst, L.ust);
       } else {
         // the delta rule reads the bypass before the decay below rewrites U
         if constexpr (MODEL == kGDN) {
@@ -1444,7 +1448,7 @@ struct Decode {
       }
     }
     if constexpr (kBypass) {
-      if (byp_regs) bypass_store(a, he, tb, tile, MODEL, SP::bf16(a), br, L.z);
+      if (byp_regs) bypass_store(a, he, tb, tile, MODEL, SP::bf16(a), br, L.z, L.ust);
     }
     // the staying window pairs: after the state's step, whose loads then go
     // out first (the pairs never touch the leaving pair's slot, which the
@@ -1487,7 +1491,7 @@ struct Decode {
           // the delta rule's new column is fp16(w_j), w as published by the
           // first row-wavefront of column j's stripe
           const float w_new = MODEL == kGDN ? L.w[(j / WC) * wrw * WC + j % WC] : 0.f;
-          part = bypass_wz_part(a, MODEL, SP::bf16(a), br, L.z, w_new);
+          part = bypass_wz_part(a, MODEL, SP::bf16(a), br, L.z, w_new, L.wst);
         }
         else if (kPW && pw_fits_all(a)) {
           // the window's w bytes from the early batch; the new pair's slot

@@ -176,7 +176,8 @@ rsq_status make_plan(const rsq_config* c, Plan& p) {
   // projections; with a bypass also the delta rule's U^T k and W (U^T k)
   G.lds = (size_t)((G.threads / 64) * G.wc + 3 * G.wrw * c->d_v + rsq::kMaxCap * (1 + G.threads / 64) +
                    (p.bypass ? rsq::kMaxCap + c->d_v : 0)) *
-          sizeof(float);
+              sizeof(float) +
+          (p.bypass && c->model == RSQ_GDN ? (size_t)(rsq::gdn_wstage_bytes(c->d_v) + rsq::gdn_ustage_bytes(c->d_k)) : 0);
   // the merge's closing products with R take 8 columns per pass (at most 8
   // columns are kept in the common case), which keeps its LDS small enough
   // for two tiles per compute unit on 128 x 128 heads

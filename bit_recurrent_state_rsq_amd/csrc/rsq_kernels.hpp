@@ -204,9 +204,18 @@ __device__ __forceinline__ void gdn_bypass_retrieval_loop(const StepArgs& a, con
 // wavefront and, for the readout term, at most kBypWCols columns per
 // partial-sum thread group (P = blockDim / d_v groups).
 constexpr int kBypCols = 4, kBypWCols = 8;
-// the delta rule's register path holds every W column of its thread's row j
-// (the retrieval's b_j runs over all of them in order)
+// the delta rule's path reads every W column of its thread's row j (the
+// retrieval's b_j runs over all of them in order): columns 0 .. n - 1, n <
+// kBypWColsGdn, go straight from memory to LDS at kernel start
 constexpr int kBypWColsGdn = 16;
+// LDS bytes of that staging area: whole 1 KB wavefront loads
+__host__ __device__ inline int gdn_wstage_bytes(int dv) { return (kBypWColsGdn * dv * 2 + 1023) / 1024 * 1024; }
+// ... and of U's columns 0 .. n - 1, each in a slot of whole 256-byte
+// wavefront loads (one dword per lane), loaded by the wavefront that reads it
+__host__ __device__ inline int gdn_ustage_slot(int dk) { return (dk * 2 + 255) / 256 * 256; }
+__host__ __device__ inline int gdn_ustage_bytes(int dk) { return kBypWColsGdn * gdn_ustage_slot(dk); }
+typedef __attribute__((address_space(1))) const void g_cvoid;
+typedef __attribute__((address_space(3))) void l_void;
 struct BypassRegs {
   // raw loaded bits: nothing is converted until bypass_store, after the
   // state's own loads have been issued. Lane l holds rows 4l .. 4l + 3.
@@ -214,9 +223,9 @@ struct BypassRegs {
   float av[4];                 // a_i
   uint32_t kb[4];              // k_i (used by the wavefront that writes column n)
   uint32_t uv[kBypCols][2];    // U_ic of the wavefront's columns (binary16 pairs)
-  // W_jc of this thread's readout columns (binary16 bits); the delta rule
-  // holds columns 0 .. kBypWColsGdn - 1 of row j in every thread of the row
-  uint32_t wv[kBypWColsGdn];
+  // W_jc of this thread's readout columns (binary16 bits; the delta rule's
+  // are in LDS)
+  uint32_t wv[kBypWCols];
   uint32_t vb;                 // v_j (column n of W is fp16(v_j); not for the delta rule)
 };
 
@@ -257,7 +266,7 @@ __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 // loads, so they all leave before the first wait. Four consecutive rows per
 // lane make each column one 8-byte load.
 __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& he, const uint8_t* tb, int tile,
-                                            int model, bool bf16, BypassRegs& br) {
+                                            int model, bool bf16, BypassRegs& br, __half* wst, uint8_t* ust) {
   const uint16_t* U = reinterpret_cast<const uint16_t*>(tb + he.bypass_u);
   const uint16_t* W = reinterpret_cast<const uint16_t*>(tb + he.bypass_w);
   // column indices clamp to the last column the step uses (U: n - 1, W: n),
@@ -275,11 +284,29 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
 #pragma unroll
     for (int r = 0; r < 4; ++r) br.av[r] = d;
   }
+  if (model == kGDN) {
+    // U's columns c = wave + nw m < n into their LDS slots at ust + c slot:
+    // one dword per lane per 256 bytes, a lane past the column reading the
+    // column's last dword (into its slot's padding)
+    const uint8_t* Ub = reinterpret_cast<const uint8_t*>(U);
+    const int cb = a.dk * 2, slot = gdn_ustage_slot(a.dk);
 #pragma unroll
-  for (int m = 0; m < kBypCols; ++m) {
-    const int c = min(wave + nw * m, ulast);
-    const uint2 t = *reinterpret_cast<const uint2*>(U + (size_t)c * a.dk + i4);
-    br.uv[m][0] = t.x, br.uv[m][1] = t.y;
+    for (int m = 0; m < kBypCols; ++m) {
+      const int c = wave + nw * m;
+      if (c < a.n) {
+        for (int t0 = 0; t0 < cb; t0 += 256) {
+          const int off = min(t0 + 4 * lane, cb - 4);
+          __builtin_amdgcn_global_load_lds((g_cvoid*)(Ub + (size_t)c * cb + off), (l_void*)(ust + (size_t)c * slot + t0), 4, 0, 0);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kBypCols; ++m) {
+      const int c = min(wave + nw * m, ulast);
+      const uint2 t = *reinterpret_cast<const uint2*>(U + (size_t)c * a.dk + i4);
+      br.uv[m][0] = t.x, br.uv[m][1] = t.y;
+    }
   }
   // readout term: thread (pp, j) takes columns pp, pp + P, ... (column n is
   // fp16(v_j), written this step: taken from v, not read back). The delta
@@ -288,8 +315,18 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
   const int P = (int)(blockDim.x / a.dv);
   const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
   if (model == kGDN) {
-#pragma unroll
-    for (int m = 0; m < kBypWColsGdn; ++m) br.wv[m] = W[(size_t)min(m, ulast) * a.dv + j];
+    // W's columns 0 .. n - 1 (column-major, contiguous) into LDS at wst: one
+    // 1 KB direct load per wavefront instruction, 16 bytes per lane at
+    // wst + 1024 c + 16 lane; a lane past W's section reads its last 16
+    // bytes instead (staged past the columns the step reads)
+    const uint8_t* Wb = reinterpret_cast<const uint8_t*>(W);
+    const int wbytes = a.n * a.dv * 2, wcap = a.cap * a.dv * 2;
+    for (int c0 = 1024 * wave; c0 < wbytes; c0 += 1024 * nw) {
+      const int off = min(c0 + 16 * lane, wcap - 16);
+      __builtin_amdgcn_global_load_lds((g_cvoid*)(Wb + off), (l_void*)(reinterpret_cast<uint8_t*>(wst) + c0), 16, 0, 0);
+    }
+    (void)P;
+    (void)pp;
     br.vb = 0u;
     return;
   }
@@ -303,24 +340,32 @@ __device__ __forceinline__ void bypass_load(const StepArgs& a, const HeadEntry& 
 // lane's rows pairwise and then wave_sum64 give the pairwise row tree. Runs
 // before the retrieval of the stored state; ends with a barrier.
 __device__ __forceinline__ void gdn_bypass_retrieval_regs(const StepArgs& a, bool bf16, const BypassRegs& br,
-                                                          float* zk, float* bz) {
+                                                          float* zk, float* bz, const __half* wst, const uint8_t* ust) {
   const int n = a.n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const bool rows_ok = 4 * lane < a.dk;
+  const int slot = gdn_ustage_slot(a.dk);
+  // this wavefront's U columns, staged by itself, have landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int m = 0; m < kBypCols; ++m) {
     const int c = wave + nw * m;
     if (c >= n) break;
+    const uint2 uw = *reinterpret_cast<const uint2*>(ust + (size_t)c * slot + 8 * min(lane, a.dk / 4 - 1));
+    const uint32_t uu[2] = {uw.x, uw.y};
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const __half u = __ushort_as_half((uint16_t)(br.uv[m][r >> 1] >> (16 * (r & 1))));
+      const __half u = __ushort_as_half((uint16_t)(uu[r >> 1] >> (16 * (r & 1))));
       p[r] = __fmul_rn(__half2float(u), in4_at(bf16, br.kb, r));
     }
     const float acc = __fadd_rn(__fadd_rn(p[0], p[1]), __fadd_rn(p[2], p[3]));
     const float z = wave_sum64(rows_ok ? acc : 0.f);
     if (lane == 0) zk[c] = z;
   }
+  // this wavefront's W staging loads have landed in LDS; after the barrier
+  // every wavefront's have
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const int P = (int)(blockDim.x / a.dv);
   const int j = threadIdx.x % a.dv, pp = threadIdx.x / a.dv;
@@ -328,7 +373,7 @@ __device__ __forceinline__ void gdn_bypass_retrieval_regs(const StepArgs& a, boo
     float b = 0.f;
 #pragma unroll
     for (int m = 0; m < kBypWColsGdn; ++m)
-      if (m < n) b = __builtin_fmaf(__half2float(__ushort_as_half((uint16_t)br.wv[m])), zk[m], b);
+      if (m < n) b = __builtin_fmaf(__half2float(wst[(size_t)m * a.dv + j]), zk[m], b);
     bz[j] = b;
   }
   (void)P;
@@ -338,7 +383,7 @@ __device__ __forceinline__ void gdn_bypass_retrieval_regs(const StepArgs& a, boo
 // Decay and store of U, the new columns of U and W, and z_c = sum_i U_ic q_i
 // in lds_z (the lane's four rows in order, then a wave reduction).
 __device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                             int model, bool bf16, BypassRegs& br, float* lds_z) {
+                                             int model, bool bf16, BypassRegs& br, float* lds_z, const uint8_t* ust) {
   uint16_t* U = reinterpret_cast<uint16_t*>(tb + he.bypass_u);
   __half* W = reinterpret_cast<__half*>(tb + he.bypass_w);
   const int n = a.n;
@@ -354,13 +399,22 @@ __device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry&
   for (int m = 0; m < kBypCols; ++m) {
     const int c = wave + nw * m;
     if (c > n) break;
-    pin(br.uv[m][0]);
-    pin(br.uv[m][1]);
+    uint32_t uu[2];
+    if (model == kGDN) {
+      // (the wavefront's own staged column; column n is written, not read)
+      const uint2 uw = c < n ? *reinterpret_cast<const uint2*>(ust + (size_t)c * gdn_ustage_slot(a.dk) + 8 * min(lane, a.dk / 4 - 1))
+                             : make_uint2(0u, 0u);
+      uu[0] = uw.x, uu[1] = uw.y;
+    } else {
+      pin(br.uv[m][0]);
+      pin(br.uv[m][1]);
+      uu[0] = br.uv[m][0], uu[1] = br.uv[m][1];
+    }
     float acc = 0.f;
     uint16_t un[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const __half u = __ushort_as_half((uint16_t)(br.uv[m][r >> 1] >> (16 * (r & 1))));
+      const __half u = __ushort_as_half((uint16_t)(uu[r >> 1] >> (16 * (r & 1))));
       const __half h = c < n ? mul_rn_half(br.av[r], u) : __float2half_rn(in4_at(bf16, br.kb, r));
       un[r] = __half_as_ushort(h);
       acc = __builtin_fmaf(__half2float(h), in4_at(bf16, br.qb, r), acc);
@@ -381,7 +435,7 @@ __device__ __forceinline__ void bypass_store(const StepArgs& a, const HeadEntry&
 // Readout term of the register path: this thread's share of (W z)_j. The
 // delta rule passes its new column's fp16(w_j) as w_new.
 __device__ __forceinline__ float bypass_wz_part(const StepArgs& a, int model, bool bf16, BypassRegs& br,
-                                                const float* lds_z, float w_new) {
+                                                const float* lds_z, float w_new, const __half* wst) {
   const int P = (int)(blockDim.x / a.dv);
   const int pp = threadIdx.x / a.dv;
   const int cnt = a.n + 1;
@@ -390,9 +444,10 @@ __device__ __forceinline__ float bypass_wz_part(const StepArgs& a, int model, bo
     // thread pp takes columns pp, pp + P, ... of its held row
 #pragma unroll
     for (int m = 0; m < kBypWColsGdn; ++m) {
-      pin(br.wv[m]);
-      const __half wh = m == a.n ? __float2half_rn(w_new) : __ushort_as_half((uint16_t)br.wv[m]);
-      if (m < cnt && m % P == pp) part = __builtin_fmaf(__half2float(wh), lds_z[m], part);
+      if (m < cnt && m % P == pp) {
+        const __half wh = m == a.n ? __float2half_rn(w_new) : wst[(size_t)m * a.dv + (threadIdx.x % a.dv)];
+        part = __builtin_fmaf(__half2float(wh), lds_z[m], part);
+      }
     }
     return part;
   }
