@@ -32,24 +32,24 @@ constexpr uint32_t kStatusNonfinite = 1u, kStatusScaleOverflow = 2u, kStatusClip
 constexpr int kMaxCap = 32;   // bypass columns a kernel can hold
 
 // OCP E4M3 (exponent bias 7, 3 mantissa bits, largest finite 448, no
-// infinities): round to nearest-even, saturate to +-448, NaN -> 0x7F with the
-// sign kept. gfx950's conversion instructions use this format: v_cvt_pk_fp8_f32
-// rounds to nearest-even, and with its input clamped to +-448 first it
-// saturates as above; v_cvt_f32_fp8 is exact. Checked against a bitwise
-// software encoder over all 2^32 float inputs and all 256 codes: the only
-// difference is the sign the encoder gives a NaN, which is set here.
+// infinities): round to nearest-even, saturate to +-448 (infinities too),
+// every NaN -> 0x7F. gfx950's conversion instructions use this format:
+// v_cvt_pk_fp8_f32 rounds to nearest-even, and with its input clamped to
+// +-448 first it saturates as above; v_cvt_f32_fp8 is exact. Checked against a
+// bitwise software encoder over all 2^32 float inputs and all 256 codes: the
+// two differ only in the byte a NaN gets, which is set here.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   const float xc = fminf(fmaxf(x, -448.f), 448.f);
   const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(xc, xc, 0, false) & 0xFFu;
-  return (x == x) ? c : (0x7Fu | ((__float_as_uint(x) >> 24) & 0x80u));
+  return (x == x) ? c : 0x7Fu;
 }
 
 // two codes at once: a in bits 0-7, b in bits 8-15
 __device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
   const float ac = fminf(fmaxf(a, -448.f), 448.f), bc = fminf(fmaxf(b, -448.f), 448.f);
   uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ac, bc, 0, false) & 0xFFFFu;
-  if (!(a == a)) c = (c & 0xFF00u) | 0x7Fu | ((__float_as_uint(a) >> 24) & 0x80u);
-  if (!(b == b)) c = (c & 0x00FFu) | ((0x7Fu | ((__float_as_uint(b) >> 24) & 0x80u)) << 8);
+  if (!(a == a)) c = (c & 0xFF00u) | 0x7Fu;
+  if (!(b == b)) c = (c & 0x00FFu) | 0x7F00u;
   return c;
 }
 

@@ -91,3 +91,52 @@ def test_attach_restores_a_window_state():
     ob = b.decode_step(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
     torch.cuda.synchronize()
     assert torch.equal(oa, ob) and torch.equal(a.buf, b.buf)
+
+
+# bf16 values around every decision of the E4M3 encoding (OCP E4M3 of
+# "Low-Bit GDN Recurrent-State Quantization ...", abstract; reading of its
+# rounding and saturation): zeros, the subnormal grid m 2^-9 and its ties,
+# the subnormal/normal boundary, ties in the normal range, the largest
+# finite value 448, the tie 464 with the NaN pattern above it, and beyond
+_E4M3_EDGES = [0.0, 2.0 ** -12, 2.0 ** -10, 2.0 ** -9, 3 * 2.0 ** -10, 5 * 2.0 ** -10, 7 * 2.0 ** -9,
+               15 * 2.0 ** -10, 2.0 ** -6, 1.0, 1.0625, 1.1875, 1.25, 3.0, 240.0, 416.0, 432.0, 440.0,
+               448.0, 456.0, 464.0, 472.0, 480.0, 496.0, 512.0, 1.0e4, 3.0e38, 1.0e-30]
+
+
+def test_window_e4m3_edge_cases():
+    """The new pair (e4m3(k_t), e4m3(fl(beta_t v_t))) byte for byte against the
+    oracle's encoder on inputs that hit every class of the conversion; v also
+    carries infinities and NaNs of both signs (v feeds only the pair and the
+    readout, so the history stays finite)."""
+    import torch
+    from oracle.window import fp8_encode, fp8_round
+    w = _w(batch=1, heads=1, d_k=128, d_v=128, pw_window=8)
+    st = make_state(w)
+    edges = np.array(_E4M3_EDGES, np.float32)
+    rng = np.random.default_rng(11)
+    kv = np.concatenate([edges, -edges])
+    k = np.concatenate([kv, (rng.standard_normal(w.d_k - kv.size) * 0.1).astype(np.float32)])
+    kb = (k.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # bf16 of k (edges are exact)
+    vb = kb.copy()
+    vb[-6:] = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7FC1, 0xFF81], np.uint16)   # +-inf, NaNs
+    qb = (rng.standard_normal(w.d_k).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    dev = lambda bits: torch.from_numpy(bits.astype(np.int16)).cuda().view(torch.bfloat16).reshape(1, 1, -1)
+    alpha = torch.full((1, 1), 0.9, dtype=torch.float32, device="cuda")
+    beta = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    st.decode_step(dev(qb), dev(kb), dev(vb), alpha, beta)
+    torch.cuda.synchronize()
+    sec = st._sections[0]
+    base = st.tile_offset(0, 0)
+    raw = st.buf.view(-1)[: st.nbytes].view(torch.uint8).cpu().numpy()
+    u_gpu = raw[base + sec["bypass_u"]: base + sec["bypass_u"] + w.d_k]
+    w_gpu = raw[base + sec["bypass_w"]: base + sec["bypass_w"] + w.d_v]
+    kf = (kb.astype(np.uint32) << 16).view(np.float32)
+    vf = (vb.astype(np.uint32) << 16).view(np.float32)     # fl(1 * v) = v
+    with np.errstate(invalid="ignore"):   # (casting the NaN inputs)
+        u_ref = fp8_encode(fp8_round(kf))
+        w_ref = fp8_encode(fp8_round(vf))
+    bad_u = np.nonzero(u_gpu != u_ref)[0]
+    bad_w = np.nonzero(w_gpu != w_ref)[0]
+    log("e4m3 edges: %d u and %d w bytes differ" % (bad_u.size, bad_w.size))
+    assert bad_u.size == 0, [(float(kf[i]), int(u_gpu[i]), int(u_ref[i])) for i in bad_u[:8]]
+    assert bad_w.size == 0, [(float(vf[i]), int(w_gpu[i]), int(w_ref[i])) for i in bad_w[:8]]
