@@ -924,18 +924,19 @@ struct Merge {
 
   // cos and sin of the rotation that zeroes H_ab (a < b) given H_aa, H_bb, H_ab;
   // index a gets (J_aa, J_ba) = (c, -sn) and b gets (J_bb, J_ab) = (c, sn)
+  // Branch-free: with d = H_bb - H_aa and e = 2 H_ab, the smaller root of
+  // t^2 + 2 (d / e) t - 1 = 0 is t = sgn(d) e / (|d| + sqrt(d^2 + e^2)) (sgn by
+  // d's sign bit), and e = 0 gives the identity. The angle to about an ulp:
+  // the rotations stay orthogonal to that order. (|d|, |e| stay far below
+  // 2^63: H is Q^T C Q scaled into binary16 range.)
   static __device__ __forceinline__ void rot_cs(float haa, float hbb, float hab, float& c, float& sn) {
-    c = 1.f;
-    sn = 0.f;
-    if (hab != 0.f) {
-      // the angle to about an ulp: the rotations stay orthogonal to that order
-      const float th = (hbb - haa) * (0.5f * __builtin_amdgcn_rcpf(hab));
-      const float at = fabsf(th);
-      const float t = (at > 1e18f) ? 0.5f * __builtin_amdgcn_rcpf(th)
-                                   : copysignf(__builtin_amdgcn_rcpf(at + __builtin_amdgcn_sqrtf(th * th + 1.f)), th);
-      c = __builtin_amdgcn_rsqf(t * t + 1.f);
-      sn = t * c;
-    }
+    const float d = hbb - haa, e = 2.f * hab;
+    const float r = __builtin_amdgcn_sqrtf(d * d + e * e);
+    const float sd = (__float_as_int(d) < 0) ? -1.f : 1.f;   // the sign bit of d
+    float t = (sd * e) * __builtin_amdgcn_rcpf(fabsf(d) + r);
+    t = (e != 0.f) ? t : 0.f;
+    c = __builtin_amdgcn_rsqf(t * t + 1.f);
+    sn = t * c;
   }
 
   // Cyclic Jacobi on the symmetric p x p matrix at H (row stride kSm), all
