@@ -57,6 +57,11 @@ namespace rsq {
 constexpr int kMergeItersWide = 4;    // p >= 8k + 8
 constexpr int kMergeItersMid = 5;     // p >= 3k + 4
 constexpr int kMergeItersNarrow = 12;
+// A basis whose last condition estimate is at most this takes two products
+// with C before it is orthonormalised again (the condition number grows by
+// at most the product's); on the workloads' residuals 128 leaves the
+// Eckart-Young excess where 8 had it and saves most tiles an orthonormalisation
+constexpr float kDoubleKappa = 128.f;
 constexpr int kJacobiSweeps = 12;  // upper bound; stops once the off-diagonal part is negligible
 constexpr int kSm = kMaxCap + 1;   // row stride of the small p x p matrices
 constexpr int kWs = kMaxCap + 4;   // row stride of the Gram / Cholesky scratch (16-byte rows)
@@ -1238,7 +1243,7 @@ struct Merge {
       // orthonormalised again (never the last one, so that the final basis
       // stays well conditioned): the condition number grows by at most the
       // product's, about the last estimate (uniform: every thread read it)
-      if (it + 1 < iters && kappa <= 8.f) {
+      if (it + 1 < iters && kappa <= kDoubleKappa) {
         float ym = 0.f;
         for (int w = 0; w < g.nw; ++w) ym = fmaxf(ym, wmax[w]);
         __syncthreads();   // the maxima are read before the next product rewrites them
