@@ -211,6 +211,71 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Lane J of each 16-lane row, to every lane of the row (DPP row_newbcast).
+template <int J>
+__device__ __forceinline__ float bc16(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xF, 0xF, true));
+}
+// acc += (lane J's src) m in one instruction (v_fmac_f32 with the broadcast on
+// src). The caller makes sure that src was not written by the two cycles
+// before (the DPP read hazard): see dpp_ready.
+template <int J>
+__device__ __forceinline__ void fmac_bc16(float& acc, float src, float m) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(m), "n"(J));
+}
+// two wait states after v was written, before a DPP instruction reads it
+__device__ __forceinline__ void dpp_ready(float& v) { asm volatile("s_nop 1" : "+v"(v)); }
+
+// Cholesky of a p x p Gram matrix (p <= 16) in one wavefront, lane i holding
+// row i: step K broadcasts the pivot and L's column K within the 16-lane row
+// (no scalar round trip), and each update is one fused multiply-add.
+template <int P8, int J>
+__device__ __forceinline__ void chol16_upd(float (&row)[P8], float lik, float nlik) {
+  if constexpr (J < P8) {
+    fmac_bc16<J>(row[J], lik, nlik);   // row_J -= L_Jk L_lk
+    chol16_upd<P8, J + 1>(row, lik, nlik);
+  }
+}
+template <int P8, int K>
+__device__ __forceinline__ void chol16(float (&row)[P8], float gii, float& dmine, int l) {
+  if constexpr (K < P8) {
+    dpp_ready(row[K]);
+    const float piv = bc16<K>(row[K]);
+    const float gkk = bc16<K>(gii);
+    const bool live = piv > 1e-6f * gkk && piv > 0.f;
+    // 1/sqrt to about an ulp: the next pass (or CholeskyQR2) removes what this one leaves
+    const float di = live ? __builtin_amdgcn_rsqf(piv) : 0.f;
+    float lik = __fmul_rn(row[K], di);
+    row[K] = lik;
+    if (l == K) dmine = di;
+    const float nlik = -lik;
+    dpp_ready(lik);
+    chol16_upd<P8, K + 1>(row, lik, nlik);
+    chol16<P8, K + 1>(row, gii, dmine, l);
+  }
+}
+// L^-1 by columns (lane l forms column l), the same way: x_I = (I == l ? 1 :
+// -sum_{t<I} L_It x_t) / L_II, with L_It (lane I's row[t]) and 1/L_II broadcast
+template <int P8, int I, int T>
+__device__ __forceinline__ void linv16_sum(const float (&row)[P8], const float (&x)[P8], float (&s4)[4]) {
+  if constexpr (T < I) {
+    fmac_bc16<I>(s4[T & 3], row[T], x[T]);
+    linv16_sum<P8, I, T + 1>(row, x, s4);
+  }
+}
+template <int P8, int I>
+__device__ __forceinline__ void linv16(const float (&row)[P8], float dmine, float (&x)[P8], int l, float* Mi, int ws) {
+  if constexpr (I < P8) {
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    linv16_sum<P8, I, 0>(row, x, s4);
+    const float su = __fadd_rn(__fadd_rn(s4[0], s4[1]), __fadd_rn(s4[2], s4[3]));
+    const float di = bc16<I>(dmine);
+    x[I] = (I == l) ? di : ((I < l) ? 0.f : -__fmul_rn(di, su));
+    if (l < P8) Mi[I * ws + l] = x[I];
+    linv16<P8, I + 1>(row, dmine, x, l, Mi, ws);
+  }
+}
+
 __device__ __forceinline__ void load_half8(const __half* p, float out[8]) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -791,10 +856,24 @@ struct Merge {
       wave_sync_lds();
       // G = L L^T, lane i holding row i
       float row[P8];
+      float dmine = 0.f;
+      if constexpr (P8 <= 16) {
+        // (unconditional reads: rows past 16 of the scratch hold nothing the
+        // first 16 lanes use)
+#pragma unroll
+        for (int c = 0; c < P8; ++c) {
+          const float v = Lr[l * kWs + c];
+          row[c] = (l < p && c < p) ? v : 0.f;
+        }
+        const float gd = Lr[l * kWs + (l & 15)];
+        const float gii = (l < p) ? gd : 0.f;
+        chol16<P8, 0>(row, gii, dmine, l);
+        float x[P8];
+        linv16<P8, 0>(row, dmine, x, l, Mi, kWs);
+      } else {
 #pragma unroll
       for (int c = 0; c < P8; ++c) row[c] = (l < p && c < p) ? Lr[l * kWs + c] : 0.f;
       const float gii = (l < p) ? Lr[l * kWs + l] : 0.f;
-      float dmine = 0.f;
 #pragma unroll
       for (int k = 0; k < P8; ++k) {
         const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(row[k]), k));
@@ -828,6 +907,7 @@ struct Merge {
           x[i] = (i == l) ? di : ((i < l) ? 0.f : -__fmul_rn(di, su));
           if (l < P8) Mi[i * kWs + l] = x[i];
         }
+      }
       }
       // condition estimate: the live diagonal entries of L are the 1/dinv
       const bool lv = l < p && dmine > 0.f;
