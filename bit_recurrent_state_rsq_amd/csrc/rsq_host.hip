@@ -564,8 +564,18 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && bf16 && g == 64) spec = 2;
   else if (sm == RSQ_SCALE_DYNAMIC && sf16 && bf16 && g == 32) spec = 3;
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && !bf16 && g == 64) spec = 4;
-  rsq::DecodeFn fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
-  const rsq_status s = launch(fn, st, a, stream, start_event, stop_event);
+  // plain states whose heads share one width take the streamed-row step
+  // where it exists (same arithmetic, fewer registers)
+  // (same arithmetic, fewer registers); its waves stage their code chunks
+  // in LDS, 512 bytes per code bit each
+  rsq::DecodeFn fn = nullptr;
+  size_t lds = 0;
+  if (feat == rsq::kFeatPlain && st->uniform && spec != 0) {
+    fn = rsq::decode_stream_for(model, st->geo.cl, spec, st->heads[0].bits);
+    if (fn) lds = st->geo.lds + (size_t)(st->geo.threads / 64) * 512 * st->heads[0].bits;
+  }
+  if (!fn) fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
+  const rsq_status s = launch(fn, st, a, stream, start_event, stop_event, lds);
   if (s != RSQ_OK) return s;
   st->t += 1;
   if (st->bypass) st->n += 1;
