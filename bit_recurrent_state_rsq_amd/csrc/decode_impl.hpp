@@ -532,6 +532,7 @@ struct Decode {
     float* bz;     // [dv]       delta rule with a bypass: b = W z
     __half* wst;   // gdn_wstage_bytes(dv)  delta rule with a bypass: W's columns, staged
     uint8_t* ust;  // gdn_ustage_bytes(dk)  ... and U's
+    uint8_t* stg;  // [nwaves][512 BITS bytes] the waves' code chunks, staged (run_piece)
   };
 
   static __device__ __forceinline__ void decays(const StepArgs& a, const HeadEntry& he, int tile, int i0,
@@ -733,6 +734,39 @@ struct Decode {
     return in_elem(SP::bf16(a), a.v, (size_t)tile * a.dv + j);
   }
 
+  // A wavefront's code chunks lie in memory as CL runs, one per column block:
+  // the RL chunks of its rows are consecutive. Staged through the wave's LDS
+  // area (the runs one after another), every load and store instruction moves
+  // contiguous 16-byte pieces of whole runs, where a lane's own chunk would
+  // take one 16-byte piece out of every 8*BITS bytes per instruction.
+  template <int BITS>
+  static __device__ __forceinline__ uint8_t* run_piece(uint8_t* tb, const StepArgs& a, int wc, int wr, int P) {
+    constexpr int PR = RL * BITS / 2;   // 16-byte pieces per run
+    const int r = P / PR, w = P - r * PR;
+    return tb + ((size_t)(wc * CL + r) * (a.dk >> 3) + wr * RL) * (8 * BITS) + 16 * w;
+  }
+  // the lane's chunk inside the staged runs
+  template <int BITS>
+  static __device__ __forceinline__ uint4* staged_chunk(uint8_t* stg, int lc, int rho) {
+    return reinterpret_cast<uint4*>(stg + (lc * RL + rho) * (8 * BITS));
+  }
+  // the new chunk back through the staged runs: each lane writes its chunk to
+  // its place in the wave's area, then stores contiguous pieces
+  template <int BITS>
+  static __device__ __forceinline__ void stage_store(const StepArgs& a, uint8_t* tb, uint8_t* stg, int wc, int wr,
+                                                     int lc, int rho, int lane, const Chunk<BITS>& ch) {
+    uint4* mine = staged_chunk<BITS>(stg, lc, rho);
+#pragma unroll
+    for (int p = 0; p < BITS / 2; ++p) mine[p] = make_uint4(ch.w[4 * p], ch.w[4 * p + 1], ch.w[4 * p + 2], ch.w[4 * p + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < BITS / 2; ++i)
+      *reinterpret_cast<uint4*>(run_piece<BITS>(tb, a, wc, wr, 64 * i + lane)) =
+          reinterpret_cast<const uint4*>(stg)[64 * i + lane];
+  }
+
   template <int BITS, bool BOOST = false>
   static __device__ __forceinline__ void body(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                               const Lds& L, uint32_t& flags, const BypassRegs* br = nullptr,
@@ -757,8 +791,21 @@ struct Decode {
     uint8_t* sp = tb + he.scales + ((size_t)G * a.dk + i0) * (sf16 ? 2 : 4);
     float x[8][8];
     float s_old[8];
+    // quantized codes: the wave's runs go to its LDS area (run_piece), and
+    // the lane's chunk is read from there once every load of the step is out.
+    // Not in the raised-priority twin: its grid is resident at once, and
+    // there the extra LDS round trip on the way in costs more than the
+    // coalesced accesses save (measured on the 64 x 16 head workload)
+    constexpr bool kStaged = !kF32 && !BOOST;
+    uint8_t* stg = kStaged ? L.stg + wave * (512 * BITS) : nullptr;
     if constexpr (kF32) {
       load_f32_chunk(cp, x);
+    } else if constexpr (kStaged) {
+#pragma unroll
+      for (int i = 0; i < BITS / 2; ++i)
+        __builtin_amdgcn_global_load_lds((g_cvoid*)run_piece<BITS>(tb, a, wc, wr, 64 * i + lane),
+                                         (l_void*)(stg + 1024 * i), 16, 0, 0);
+      load_scales8(sf16, sp, s_old);
     } else {
       Chunk<BITS> ch;
       load_chunk<BITS>(cp, ch);
@@ -797,6 +844,17 @@ struct Decode {
     if constexpr (!(FEAT == kFeatBdr || kYoked || kDiag)) __builtin_amdgcn_sched_barrier(0);
     // the loads are out: back to the normal issue priority
     if constexpr (BOOST) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kStaged) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      Chunk<BITS> ch;
+      const uint4* mine = staged_chunk<BITS>(stg, lc, rho);
+#pragma unroll
+      for (int p = 0; p < BITS / 2; ++p) {
+        const uint4 u = mine[p];
+        ch.w[4 * p] = u.x, ch.w[4 * p + 1] = u.y, ch.w[4 * p + 2] = u.z, ch.w[4 * p + 3] = u.w;
+      }
+      unpack_scaled(ch, x);
+    }
 
     // per-row multipliers: c1/F (decay) and k s / F (retrieval). Dividing by
     // F = 1/16 (4 bits) is exact unless it overflows (not for binary16 steps);
@@ -1247,7 +1305,8 @@ struct Decode {
           pwp->be = dwp.be;
         }
       }
-      store_chunk<BITS>(cp, out);
+      if constexpr (kStaged) stage_store<BITS>(a, tb, stg, wc, wr, lc, rho, lane, out);
+      else store_chunk<BITS>(cp, out);
       const bool store_s = smode != kScalePersistent || grew_any;
       if constexpr (kSplit8) {
         // each group lane stores its own row
@@ -1735,23 +1794,6 @@ struct Decode {
     return SP::smode(a) != kScalePersistent || grew_any;
   }
 
-  // A wavefront's code chunks lie in memory as CL runs, one per column block:
-  // the RL chunks of its rows are consecutive. Staged through the wave's LDS
-  // area (the runs one after another), every load and store instruction moves
-  // contiguous 16-byte pieces of whole runs, where a lane's own chunk would
-  // take one 16-byte piece out of every 8*BITS bytes per instruction.
-  template <int BITS>
-  static __device__ __forceinline__ uint8_t* run_piece(uint8_t* tb, const StepArgs& a, int wc, int wr, int P) {
-    constexpr int PR = RL * BITS / 2;   // 16-byte pieces per run
-    const int r = P / PR, w = P - r * PR;
-    return tb + ((size_t)(wc * CL + r) * (a.dk >> 3) + wr * RL) * (8 * BITS) + 16 * w;
-  }
-  // the lane's chunk inside the staged runs
-  template <int BITS>
-  static __device__ __forceinline__ uint4* staged_chunk(uint8_t* stg, int lc, int rho) {
-    return reinterpret_cast<uint4*>(stg + (lc * RL + rho) * (8 * BITS));
-  }
-
   template <int BITS>
   static __device__ __forceinline__ void body_stream(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
                                                      const Lds& L, uint32_t& flags, uint8_t* stg) {
@@ -1814,19 +1856,7 @@ struct Decode {
     const bool store_s = !wave_any(bad)
         ? stream_passes<BITS, false>(a, tile, L, flags, ch, so, c1p, kf, qf, wv, lane, wrw, wr, j0, s2)
         : stream_passes<BITS, true>(a, tile, L, flags, ch, so, c1p, kf, qf, wv, lane, wrw, wr, j0, s2);
-    {
-      // the new chunk back through the staged runs
-      uint4* mine = staged_chunk<BITS>(stg, lc, rho);
-#pragma unroll
-      for (int p = 0; p < BITS / 2; ++p) mine[p] = make_uint4(ch.w[4 * p], ch.w[4 * p + 1], ch.w[4 * p + 2], ch.w[4 * p + 3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < BITS / 2; ++i)
-        *reinterpret_cast<uint4*>(run_piece<BITS>(tb, a, wc, wr, 64 * i + lane)) =
-            reinterpret_cast<const uint4*>(stg)[64 * i + lane];
-    }
+    stage_store<BITS>(a, tb, stg, wc, wr, lc, rho, lane, ch);
     if constexpr (SP::GL == 8) {
       // each group lane stores its own row
       if (store_s) {
@@ -1858,11 +1888,9 @@ struct Decode {
     uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
     const int wrw = a.dk / WR;
     const int nw = blockDim.x >> 6;
-    // each wave's staged code runs (512 BITS bytes) first, then the areas
-    // of the register-resident step
-    uint8_t* stg = reinterpret_cast<uint8_t*>(lds) + (threadIdx.x >> 6) * (512 * BITS);
+    uint8_t* stg = reinterpret_cast<uint8_t*>(lds) + a.lds_stage + (threadIdx.x >> 6) * (512 * BITS);
     Lds L{};
-    L.w = lds + nw * (128 * BITS);
+    L.w = lds;
     L.up = L.w + nw * WC;
     L.op = L.up + 2 * wrw * a.dv;
     uint32_t flags = 0;
@@ -1898,6 +1926,7 @@ struct Decode {
     L.bz = L.zk + kMaxCap;                    // [dv]
     L.wst = reinterpret_cast<__half*>(L.bz + a.dv);
     L.ust = reinterpret_cast<uint8_t*>(L.wst) + gdn_wstage_bytes(a.dv);
+    L.stg = reinterpret_cast<uint8_t*>(lds) + a.lds_stage;
     uint32_t flags = 0;
 
     // bypass: its loads join the state's (values held in registers) when

@@ -84,6 +84,7 @@ struct rsq_state {
   bool uniform = false; // every head's table entry alike up to its offset
   bool bypass = false;
   bool all32 = false;
+  int max_bits = 0;     // widest head: a decode wavefront stages 512 bytes per code bit in LDS
   uint64_t hash = 0;
   Geometry geo{};
 };
@@ -412,6 +413,8 @@ rsq_status rsq_state_alloc(const rsq_config* cfg, void* dev_buf, size_t buf_byte
                   e.head_offset == (uint64_t)h * p.heads[1].head_offset;
   }
   st->all32 = p.all32;
+  st->max_bits = 0;
+  for (const HeadEntry& e : p.heads) st->max_bits = std::max(st->max_bits, (int)e.bits);
   st->hash = p.hash;
   st->geo = p.geo;
   hipStream_t hs = (hipStream_t)stream;
@@ -566,15 +569,19 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && !bf16 && g == 64) spec = 4;
   // plain states whose heads share one width take the streamed-row step
   // where it exists (same arithmetic, fewer registers)
-  // (same arithmetic, fewer registers); its waves stage their code chunks
-  // in LDS, 512 bytes per code bit each
+  // (same arithmetic, fewer registers)
   rsq::DecodeFn fn = nullptr;
-  size_t lds = 0;
-  if (feat == rsq::kFeatPlain && st->uniform && spec != 0) {
+  if (feat == rsq::kFeatPlain && st->uniform && spec != 0)
     fn = rsq::decode_stream_for(model, st->geo.cl, spec, st->heads[0].bits);
-    if (fn) lds = st->geo.lds + (size_t)(st->geo.threads / 64) * 512 * st->heads[0].bits;
-  }
   if (!fn) fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
+  // quantized states: every wavefront stages its code chunks in LDS (512
+  // bytes per code bit), after the step's own areas
+  size_t lds = 0;
+  if (!st->all32) {
+    const size_t stage = (st->geo.lds + 15) & ~(size_t)15;
+    a.lds_stage = (int32_t)stage;
+    lds = stage + (size_t)(st->geo.threads / 64) * 512 * st->max_bits;
+  }
   const rsq_status s = launch(fn, st, a, stream, start_event, stop_event, lds);
   if (s != RSQ_OK) return s;
   st->t += 1;

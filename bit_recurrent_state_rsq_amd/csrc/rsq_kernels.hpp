@@ -51,6 +51,9 @@ struct StepArgs {
   HeadEntry uni;
   // bypass merge: columns per pass of its closing products with R
   int32_t merge_chunk;
+  // decode steps of quantized states stage each wavefront's code chunks in
+  // LDS (512 bytes per code bit and wavefront) from this byte offset on
+  int32_t lds_stage;
 };
 
 // Head table entry of head h.
