@@ -793,10 +793,12 @@ struct Decode {
     float s_old[8];
     // quantized codes: the wave's runs go to its LDS area (run_piece), and
     // the lane's chunk is read from there once every load of the step is out.
-    // Not in the raised-priority twin: its grid is resident at once, and
-    // there the extra LDS round trip on the way in costs more than the
-    // coalesced accesses save (measured on the 64 x 16 head workload)
-    constexpr bool kStaged = !kF32 && !BOOST;
+    // Not in the raised-priority twin, whose grid is resident at once, nor
+    // with a bypass (those grids fit at once too): there the extra LDS round
+    // trip on the way in costs more than the coalesced accesses save
+    // (measured on the 64 x 16 head workloads with and without a bypass, and
+    // on the GLA 32 x 8 head one)
+    constexpr bool kStaged = !kF32 && !BOOST && !kBypass;
     uint8_t* stg = kStaged ? L.stg + wave * (512 * BITS) : nullptr;
     if constexpr (kF32) {
       load_f32_chunk(cp, x);

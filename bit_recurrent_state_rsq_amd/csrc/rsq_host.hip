@@ -574,10 +574,10 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   if (feat == rsq::kFeatPlain && st->uniform && spec != 0)
     fn = rsq::decode_stream_for(model, st->geo.cl, spec, st->heads[0].bits);
   if (!fn) fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
-  // quantized states: every wavefront stages its code chunks in LDS (512
-  // bytes per code bit), after the step's own areas
+  // quantized states without a bypass: every wavefront stages its code
+  // chunks in LDS (512 bytes per code bit), after the step's own areas
   size_t lds = 0;
-  if (!st->all32) {
+  if (!st->all32 && !st->bypass) {
     const size_t stage = (st->geo.lds + 15) & ~(size_t)15;
     a.lds_stage = (int32_t)stage;
     lds = stage + (size_t)(st->geo.threads / 64) * 512 * st->max_bits;
