@@ -3,8 +3,8 @@
 The same distributions as gen.step_inputs, drawn by torch on the GPU so that
 long full-size runs (thousands of steps of a 16384-tile workload) need no
 host-side generation. The stream differs from gen.step_inputs (numpy
-draws), so these inputs are for runs that compare two device states with each
-other, never for comparisons with the oracle.
+draws): a comparison with the oracle that uses these inputs hands the oracle
+the drawn values themselves (copied to the host), never a host re-draw.
 
   q, k   Gaussian, L2-normalised in fp32 (Mamba2: N(0,1)/sqrt(d_k)), then
          rounded to the workload's input dtype (bf16: torch's RNE)

@@ -267,6 +267,31 @@ def check_merge_factors(post, md, k, what=""):
     return worst
 
 
+class DeviceInputs:
+    """Fresh inputs at every step, drawn on the device by the shared input
+    generator (rsq_workloads.gen_device: the workload's distributions, torch's
+    generator, no arithmetic of the method). The GPU step takes the full
+    device tensors; the oracle gets the sampled tiles' values, copied back to
+    the host exactly (bf16 values widen to fp32 without rounding)."""
+
+    def __init__(self, w):
+        self.w = w
+        self.a_log = static_params(w).get("a_log")
+
+    def at_device(self, t, tiles):
+        import torch
+        from rsq_workloads.gen_device import device_step_inputs
+        d = device_step_inputs(self.w, t, a_log=self.a_log)
+        dev = {k: v for k, v in d.items() if v is not None}
+        T = self.w.tiles
+        idx = torch.as_tensor(list(tiles), device="cuda", dtype=torch.long)
+        sub = {}
+        for name, x in dev.items():
+            rows = x.reshape(T, -1)[idx].float().cpu().numpy()
+            sub[name] = (rows[:, 0] if x.dim() == 2 else rows)[None]
+        return dev, sub
+
+
 def run_horizon(w, steps, tiles, pool=None, st=None, log_every=256):
     """Every step of the horizon on the sampled tiles, with the oracle kept
     in step (reconciled only at forgiven elements and at merges' factors),
@@ -287,9 +312,12 @@ def run_horizon(w, steps, tiles, pool=None, st=None, log_every=256):
     num = den = 0.0
     worst_merge = 0.0
     for t in range(1, steps + 1):
-        inp = pool.at(t) if pool is not None else step_inputs(w, t, static)
-        dev = to_device(inp, w)
-        new, o_ref, diag = ostep(ost, sub_inputs(inp, w, tiles), sw, oracle.F32, ss)
+        if isinstance(pool, DeviceInputs):
+            dev, sub = pool.at_device(t, tiles)
+        else:
+            inp = pool.at(t) if pool is not None else step_inputs(w, t, static)
+            dev, sub = to_device(inp, w), sub_inputs(inp, w, tiles)
+        new, o_ref, diag = ostep(ost, sub, sw, oracle.F32, ss)
         o = gpu_step(st, dev)
         post = st.read_tiles(tiles)
         o_gpu = o.reshape(T, -1)[tiles].cpu().numpy()
