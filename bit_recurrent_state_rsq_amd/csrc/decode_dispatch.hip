@@ -10,13 +10,4 @@ DecodeFn decode_kernel_for(int model, int cl, int feat, int spec) {
     default: return decode_gdn(cl, feat, spec);
   }
 }
-
-DecodeFn decode_stream_for(int model, int cl, int spec, int bits) {
-  switch (model) {
-    case kRetNet: return decode_stream_retnet(cl, spec, bits);
-    case kMamba2: return decode_stream_mamba2(cl, spec, bits);
-    case kGLA: return decode_stream_gla(cl, spec, bits);
-    default: return nullptr;
-  }
-}
 }  // namespace rsq

@@ -3,5 +3,4 @@
 
 namespace rsq {
 DecodeFn decode_gla(int cl, int feat, int spec) { return decode_pick_cl<kGLA>(cl, feat, spec); }
-DecodeFn decode_stream_gla(int cl, int spec, int bits) { return decode_stream_pick<kGLA>(cl, spec, bits); }
 }  // namespace rsq

@@ -1457,455 +1457,6 @@ struct Decode {
       W[j] = (uint8_t)f32_to_e4m3(__fmul_rn(be, in_elem(bf16, a.v, (size_t)tile * a.dv + j)));
   }
 
-  // ------------------------------------------------------------ streamed rows
-  // Rows without the delta rule (RetNet, Mamba2, GLA) need no sum over the
-  // tile before their update, so a lane can take its eight rows one at a time
-  // and hold one row of values instead of 64. The first pass forms each row
-  // (unpack, decay, update), adds it to the readout and keeps only the row's
-  // maximum; after the scale rule the second pass forms the rows again with
-  // the same operations (so the same values) and requantizes them, writing
-  // each row's code words over the words it was read from. The decay and
-  // update run twice, but the step needs about half the registers: twice as
-  // many wavefronts stay resident, twice as many tiles' loads are in flight,
-  // and the bytes in flight are what bound these steps. Same arithmetic as
-  // the register-resident step: bit for bit the same codes, steps and o.
-  // Compile-time group sizes of 32 or 64 columns only (GL = 4 or 8 lanes).
-
-  // row r of the lane's chunk as F * c
-  template <int BITS>
-  static __device__ __forceinline__ void unpack_row(const Chunk<BITS>& ch, int r, float c[8]) {
-    if constexpr (BITS == 4) {
-      const uint32_t w = ch.w[r], hi = w >> 4;
-      c[0] = cvt_off_byte<0>(w);
-      c[1] = cvt_off_byte<1>(w);
-      c[2] = cvt_off_byte<2>(w);
-      c[3] = cvt_off_byte<3>(w);
-      c[4] = cvt_off_byte<0>(hi);
-      c[5] = cvt_off_byte<1>(hi);
-      c[6] = cvt_off_byte<2>(hi);
-      c[7] = cvt_off_byte<3>(hi);
-    } else if constexpr (BITS == 8) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        c[b] = (float)(int8_t)(ch.w[2 * r] >> (8 * b));
-        c[b + 4] = (float)(int8_t)(ch.w[2 * r + 1] >> (8 * b));
-      }
-    } else {
-      const uint32_t cw = ch.w[8 + (r >> 1)] >> ((r & 1) * 4);
-      const uint32_t lo = ((ch.w[r] << 4) & 0xF0F0F0F0u) | ((cw << 2) & 0x0C0C0C0Cu);
-      const uint32_t hi = (ch.w[r] & 0xF0F0F0F0u) | (cw & 0x0C0C0C0Cu);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        c[b] = (float)(int8_t)(lo >> (8 * b));
-        c[b + 4] = (float)(int8_t)(hi >> (8 * b));
-      }
-    }
-  }
-
-  // rows 2p and 2p+1 of t (magic + code, Fmt) packed over their own words
-  template <int BITS>
-  static __device__ __forceinline__ void pack_rows2(const float t[2][8], int p, Chunk<BITS>& ch) {
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t q[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = (__float_as_uint(t[h][k + 4]) << 4) | __float_as_uint(t[h][k]);
-        ch.w[2 * p + h] = (lo_pair(q[0], q[1]) | hi_pair(q[2], q[3])) ^ 0x88888888u;
-      }
-    } else if constexpr (BITS == 8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        ch.w[2 * (2 * p + h)] = low_bytes(t[h][0], t[h][1], t[h][2], t[h][3]);
-        ch.w[2 * (2 * p + h) + 1] = low_bytes(t[h][4], t[h][5], t[h][6], t[h][7]);
-      }
-    } else {
-      uint32_t Lb[2], Hb[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        Lb[h] = low_bytes(t[h][0], t[h][1], t[h][2], t[h][3]);
-        Hb[h] = low_bytes(t[h][4], t[h][5], t[h][6], t[h][7]);
-        ch.w[2 * p + h] = bfi(0x0F0F0F0Fu, Lb[h] >> 2, Hb[h] << 2);
-      }
-      const uint32_t x = bfi(0x03030303u, Lb[0], Hb[0] << 2);
-      const uint32_t y = bfi(0x03030303u, Lb[1], Hb[1] << 2);
-      ch.w[8 + p] = bfi(0x0F0F0F0Fu, x, y << 4);
-    }
-  }
-
-  // q or k of the lane's eight rows as loaded: bf16 inputs stay as their four
-  // raw words (converted where a row uses them), fp32 inputs as eight floats
-  static constexpr bool kInBf16 = SPEC != kSpecDynF32F32 && SPEC != kSpecGeneric;
-  struct In8 {
-    uint32_t w[kInBf16 ? 4 : 8];
-    __device__ __forceinline__ float operator[](int i) const {
-      if constexpr (kInBf16) return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
-      else return __uint_as_float(w[i]);
-    }
-  };
-  static __device__ __forceinline__ In8 load_in8(const void* base, size_t idx) {
-    In8 r;
-    if constexpr (kInBf16) {
-      const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-      r.w[0] = u.x, r.w[1] = u.y, r.w[2] = u.z, r.w[3] = u.w;
-    } else {
-      const uint4* f = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(base) + idx);
-      const uint4 u = f[0], v = f[1];
-      r.w[0] = u.x, r.w[1] = u.y, r.w[2] = u.z, r.w[3] = u.w;
-      r.w[4] = v.x, r.w[5] = v.y, r.w[6] = v.z, r.w[7] = v.w;
-    }
-    return r;
-  }
-
-  // x of row r: fma(k_r, v_j, fl(F c_rj * c1p_r)); LONG: the exact long form
-  // fl(fl(F c_rj / F) * c1_r) for a multiplier whose c1/F is not exact
-  template <int BITS, bool LONG>
-  static __device__ __forceinline__ void stream_row(const Chunk<BITS>& ch, int r, float c1p, float k,
-                                                    const float wv[8], float x[8]) {
-    constexpr float invF = 1.f / Fmt<BITS>::F;
-    unpack_row<BITS>(ch, r, x);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float xc = LONG ? __fmul_rn(x[j], invF) : x[j];
-      x[j] = __builtin_fmaf(k, wv[j], __fmul_rn(xc, c1p));
-    }
-  }
-
-  // The scale rule from the lane's row maxima lm (the same reduce-scatter as
-  // the register-resident step: a group of 32 columns is a lane quad whose
-  // lanes settle two rows each, one of 64 is 8 lanes settling one row each).
-  // so: the old steps of the lane's own rows (stream_own_steps). Returns the
-  // reciprocals of all eight rows in inv and the lane's own rows' steps in s2.
-  static __device__ __forceinline__ void stream_own_steps(const float s_old[8], int lane, float so[2]) {
-    if constexpr (SP::GL == 4) {
-      const bool h2 = (lane & 2) != 0, h1 = (lane & 1) != 0;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) so[k] = h2 ? (h1 ? s_old[6 + k] : s_old[4 + k]) : (h1 ? s_old[2 + k] : s_old[k]);
-    } else {
-      const int q = lane & 7;
-      const bool h4 = (q & 4) != 0, h2 = (q & 2) != 0, h1 = (q & 1) != 0;
-      const float a4 = h4 ? s_old[4] : s_old[0], b4 = h4 ? s_old[5] : s_old[1];
-      const float c4 = h4 ? s_old[6] : s_old[2], d4 = h4 ? s_old[7] : s_old[3];
-      const float lo2 = h2 ? c4 : a4, hi2 = h2 ? d4 : b4;
-      so[0] = so[1] = h1 ? hi2 : lo2;
-    }
-  }
-  template <int BITS>
-  static __device__ __forceinline__ void stream_settle(const StepArgs& a, const float lm[8], const float so[2],
-                                                       int lane, float inv[8], float s2[2], bool& tiny,
-                                                       bool& grew_any, uint32_t& flags) {
-    constexpr int qmax = Fmt<BITS>::qmax;
-    constexpr float qmaxf = (float)qmax;
-    const bool sf16 = SP::sf16(a);
-    const int smode = SP::smode(a);
-    tiny = false;
-    grew_any = true;
-    if constexpr (SP::GL == 4) {
-      const bool h2 = (lane & 2) != 0, h1 = (lane & 1) != 0;
-      uint32_t kp[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t mine = __float_as_uint(h2 ? lm[4 + k] : lm[k]);
-        const uint32_t other = __float_as_uint(h2 ? lm[k] : lm[4 + k]);
-        kp[k] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x4E, 0xF, 0xF, false));
-      }
-      float m2[2], ratio[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t mine = h1 ? kp[2 + k] : kp[k], other = h1 ? kp[k] : kp[2 + k];
-        m2[k] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0xB1, 0xF, 0xF, false)));
-      }
-      if (smode == kScalePersistent) {
-        const float trig_q = __fmul_rn(a.trigger, qmaxf);
-        bool grew[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          grew[k] = m2[k] > __fmul_rn(trig_q, so[k]);
-          s2[k] = so[k];
-        }
-        grew_any = wave_any(grew[0] || grew[1]);
-        if (grew_any) {
-          div_qmax2<qmax>(m2, ratio);
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-            if (grew[k]) s2[k] = sf16 ? __half2float(__float2half_rn(ratio[k])) : ratio[k];
-        }
-      } else {
-        div_qmax2<qmax>(m2, ratio);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) s2[k] = sf16 ? __half2float(__float2half_rn(ratio[k])) : ratio[k];
-      }
-      const float s_lo = min_nc(s2[0], s2[1]), s_hi = max_nc(s2[0], s2[1]);
-      const bool regular = sf16 ? (s_lo >= 0x1p-14f && s_hi <= 65504.f) : (s_lo >= 0x1p-100f && s_hi <= 0x1p100f);
-      float iv[2];
-#pragma unroll
-      for (int k = 0; k < 2; ++k) iv[k] = sf16 ? recip_f16val(s2[k]) : 1.0f / s2[k];
-      if (!wave_all(regular)) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          if (s2[k] == 0.f || !(s2[k] <= 3.4e38f)) iv[k] = 0.f;
-        const float imax = max_nc(iv[0], iv[1]);
-        if (!(s_hi <= 3.4e38f)) flags |= kStatusScaleOverflow;
-        tiny = !(s_hi <= 3.4e38f) || !(imax <= (sf16 ? 16384.f : 0x1p100f));
-      }
-      inv[0] = dpp_quad_bcast<0>(iv[0]);
-      inv[1] = dpp_quad_bcast<0>(iv[1]);
-      inv[2] = dpp_quad_bcast<1>(iv[0]);
-      inv[3] = dpp_quad_bcast<1>(iv[1]);
-      inv[4] = dpp_quad_bcast<2>(iv[0]);
-      inv[5] = dpp_quad_bcast<2>(iv[1]);
-      inv[6] = dpp_quad_bcast<3>(iv[0]);
-      inv[7] = dpp_quad_bcast<3>(iv[1]);
-    } else {
-      static_assert(SP::GL == 8, "streamed rows take groups of 32 or 64 columns");
-      const int q = lane & 7;
-      const bool h4 = (q & 4) != 0, h2 = (q & 2) != 0, h1 = (q & 1) != 0;
-      uint32_t k4[4], k2[2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t mine = __float_as_uint(h4 ? lm[4 + r] : lm[r]);
-        const uint32_t other = __float_as_uint(h4 ? lm[r] : lm[4 + r]);
-        k4[r] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x141, 0xF, 0xF, false));
-      }
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const uint32_t mine = h2 ? k4[2 + r] : k4[r], other = h2 ? k4[r] : k4[2 + r];
-        k2[r] = max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0x4E, 0xF, 0xF, false));
-      }
-      float m1[2], ratio[2];
-      {
-        const uint32_t mine = h1 ? k2[1] : k2[0], other = h1 ? k2[0] : k2[1];
-        m1[0] = __uint_as_float(max(mine, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)other, 0xB1, 0xF, 0xF, false)));
-        m1[1] = m1[0];
-      }
-      if (smode == kScalePersistent) {
-        const float trig_q = __fmul_rn(a.trigger, qmaxf);
-        const bool grew = m1[0] > __fmul_rn(trig_q, so[0]);
-        s2[0] = so[0];
-        grew_any = wave_any(grew);
-        if (grew_any) {
-          div_qmax2<qmax>(m1, ratio);
-          if (grew) s2[0] = sf16 ? __half2float(__float2half_rn(ratio[0])) : ratio[0];
-        }
-      } else {
-        div_qmax2<qmax>(m1, ratio);
-        s2[0] = sf16 ? __half2float(__float2half_rn(ratio[0])) : ratio[0];
-      }
-      s2[1] = s2[0];
-      const float sv = s2[0];
-      const bool regular = sf16 ? (sv >= 0x1p-14f && sv <= 65504.f) : (sv >= 0x1p-100f && sv <= 0x1p100f);
-      float iv = sf16 ? recip_f16val(sv) : 1.0f / sv;
-      if (!wave_all(regular)) {
-        if (sv == 0.f || !(sv <= 3.4e38f)) iv = 0.f;
-        if (!(sv <= 3.4e38f)) flags |= kStatusScaleOverflow;
-        tiny = !(sv <= 3.4e38f) || !(iv <= (sf16 ? 16384.f : 0x1p100f));
-      }
-      float g2[2], g4v[4];
-      const float p1 = dpp_xor1(iv);
-      g2[0] = h1 ? p1 : iv;
-      g2[1] = h1 ? iv : p1;
-      const float p2a = dpp_xor2(g2[0]), p2b = dpp_xor2(g2[1]);
-      g4v[0] = h2 ? p2a : g2[0];
-      g4v[1] = h2 ? p2b : g2[1];
-      g4v[2] = h2 ? g2[0] : p2a;
-      g4v[3] = h2 ? g2[1] : p2b;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = swz_xor(g4v[r], 4);
-        inv[r] = h4 ? pr : g4v[r];
-        inv[4 + r] = h4 ? g4v[r] : pr;
-      }
-    }
-  }
-
-  // the second pass; clamp: clip the codes to the range (tiny steps, a
-  // persistent trigger above 1), returning whether any was clipped. (Taking
-  // the clamp as a template argument duplicates the pass, and the register
-  // allocator then spills.)
-  template <int BITS, bool LONG>
-  static __device__ __forceinline__ bool stream_pass2(Chunk<BITS>& ch, const float c1p[8], const In8& kf,
-                                                      const float wv[8], const float inv[8], bool clamp) {
-    constexpr float magic = Fmt<BITS>::magic, lo_t = Fmt<BITS>::lo_t, hi_t = Fmt<BITS>::hi_t;
-    bool clipped = false;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float t[2][8];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int i = 2 * p + h;
-        stream_row<BITS, LONG>(ch, i, c1p[i], kf[i], wv, t[h]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t[h][j] = __builtin_fmaf(t[h][j], inv[i], magic);
-        if (clamp) {
-          clipped = clipped || max8(t[h]) > hi_t || min8(t[h]) < lo_t;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) t[h][j] = med3_nc(t[h][j], lo_t, hi_t);
-        }
-      }
-      pack_rows2<BITS>(t, p, ch);
-    }
-    return clipped;
-  }
-
-  // both passes, after the loads (LONG: the exact long form of the decay)
-  template <int BITS, bool LONG>
-  static __device__ __forceinline__ bool stream_passes(const StepArgs& a, int tile, const Lds& L, uint32_t& flags,
-                                                       Chunk<BITS>& ch, const float so[2], const float c1p[8],
-                                                       const In8& kf, const In8& qf, const float wv[8],
-                                                       int lane, int wrw, int wr, int j0, float s2[2]) {
-    // pass 1: rows in order; the readout's chain over the lane's rows is the
-    // register-resident step's (row 0's product, then one FMA per row)
-    float o8[8], lm[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x[8];
-      stream_row<BITS, LONG>(ch, i, c1p[i], kf[i], wv, x);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o8[j] = i == 0 ? __fmul_rn(qf[0], x[j]) : __builtin_fmaf(qf[i], x[j], o8[j]);
-      lm[i] = absmax8(x);
-    }
-    xtree<NB>(o8, lane);
-    {
-      const bool writer = NB < 4 || ((lane >> 2) & 1) == 0;
-      if (wrw == 1) {
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s) {
-          const float o = o8[s];
-          if (!(fabsf(o) <= 3.4e38f)) flags |= kStatusNonfinite;
-          if (writer) a.o[(size_t)tile * a.dv + j0 + xtree_col<NB>(s, lane)] = o;
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NSLOT; ++s)
-          if (writer) L.op[wr * a.dv + j0 + xtree_col<NB>(s, lane)] = o8[s];
-      }
-    }
-    float inv[8];
-    bool tiny, grew_any;
-    stream_settle<BITS>(a, lm, so, lane, inv, s2, tiny, grew_any, flags);
-    const bool clamp = wave_any(tiny) || (SP::smode(a) == kScalePersistent && a.trigger > 1.f);
-    // the code words pass through an empty asm, so the compiler cannot keep
-    // pass 1's values alive for pass 2 instead of forming them again
-#pragma unroll
-    for (int k = 0; k < Chunk<BITS>::kWords; ++k) asm volatile("" : "+v"(ch.w[k]));
-    // pass 2: rows again in pairs (a 6-bit chunk keeps the low bits of two
-    // rows in one word), requantized and packed in place
-    const bool clipped = stream_pass2<BITS, LONG>(ch, c1p, kf, wv, inv, clamp);
-    if (clipped) flags |= kStatusClipped;
-    // persistent steps are stored only when a group of the wavefront grew
-    return SP::smode(a) != kScalePersistent || grew_any;
-  }
-
-  template <int BITS>
-  static __device__ __forceinline__ void body_stream(const StepArgs& a, const HeadEntry& he, uint8_t* tb, int tile,
-                                                     const Lds& L, uint32_t& flags, uint8_t* stg) {
-    const bool bf16 = SP::bf16(a), sf16 = SP::sf16(a);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int wrw = a.dk / WR;
-    const int wr = wave % wrw, wc = wave / wrw;
-    const int lc = lane % CL, lr = lane / CL;
-    const int rho = (int)(__builtin_bitreverse32((uint32_t)lr) >> (32 - NB));
-    const int i0 = wr * WR + 8 * rho;
-    const int j0 = wc * WC + 8 * lc;
-    constexpr int glog = SP::GL == 4 ? 5 : 6;
-    const int G = j0 >> glog;
-    constexpr float invF = 1.f / Fmt<BITS>::F;
-    uint8_t* sp = tb + he.scales + ((size_t)G * a.dk + i0) * (sf16 ? 2 : 4);
-    Chunk<BITS> ch;
-    float s_old[8], dec[8], wv[8];
-    // the wave's runs into its LDS area, 1 KB per instruction
-#pragma unroll
-    for (int i = 0; i < BITS / 2; ++i)
-      __builtin_amdgcn_global_load_lds((g_cvoid*)run_piece<BITS>(tb, a, wc, wr, 64 * i + lane), (l_void*)(stg + 1024 * i),
-                                       16, 0, 0);
-    load_scales8(sf16, sp, s_old);
-    const In8 qf = load_in8(a.q, (size_t)tile * a.dk + i0);
-    const In8 kf = load_in8(a.k, (size_t)tile * a.dk + i0);
-    decays(a, he, tile, i0, dec);
-    load8(bf16, a.v, (size_t)tile * a.dv + j0, wv);
-    // every load of the step is out before any arithmetic; then the lane's
-    // chunk comes from the staged runs
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    {
-      const uint4* mine = staged_chunk<BITS>(stg, lc, rho);
-#pragma unroll
-      for (int p = 0; p < BITS / 2; ++p) {
-        const uint4 u = mine[p];
-        ch.w[4 * p] = u.x, ch.w[4 * p + 1] = u.y, ch.w[4 * p + 2] = u.z, ch.w[4 * p + 3] = u.w;
-      }
-    }
-    // the decay multiplier c1/F, exact unless it overflows (4 bits, fp32
-    // steps) or is subnormal (6 bits); the exact long form runs otherwise
-    constexpr bool kUp = BITS == 4, kDown = BITS == 6;
-    float c1p[8];
-    bool bad = false;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float c1 = __fmul_rn(dec[i], s_old[i]);
-      c1p[i] = (kUp || kDown) ? __fmul_rn(c1, invF) : c1;
-      if constexpr (kDown) bad = bad || subnormal(c1p[i]);
-      if constexpr (kUp) {
-        if (!sf16) bad = bad || !(fabsf(c1p[i]) <= 3.4e38f);
-      }
-    }
-    if (wave_any(bad)) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c1p[i] = __fmul_rn(dec[i], s_old[i]);
-    }
-    float so[2], s2[2];
-    stream_own_steps(s_old, lane, so);
-    const bool store_s = !wave_any(bad)
-        ? stream_passes<BITS, false>(a, tile, L, flags, ch, so, c1p, kf, qf, wv, lane, wrw, wr, j0, s2)
-        : stream_passes<BITS, true>(a, tile, L, flags, ch, so, c1p, kf, qf, wv, lane, wrw, wr, j0, s2);
-    stage_store<BITS>(a, tb, stg, wc, wr, lc, rho, lane, ch);
-    if constexpr (SP::GL == 8) {
-      // each group lane stores its own row
-      if (store_s) {
-        uint8_t* sp1 = sp + (size_t)(lane & 7) * (sf16 ? 2 : 4);
-        if (sf16) *reinterpret_cast<uint16_t*>(sp1) = __half_as_ushort(__float2half_rn(s2[0]));
-        else *reinterpret_cast<float*>(sp1) = s2[0];
-      }
-    } else {
-      // each quad lane stores its own two rows
-      uint8_t* sp2 = sp + (size_t)(2 * (lane & 3)) * (sf16 ? 2 : 4);
-      if (store_s) {
-        if (sf16) {
-          const uint32_t lo = __half_as_ushort(__float2half_rn(s2[0])), hi = __half_as_ushort(__float2half_rn(s2[1]));
-          *reinterpret_cast<uint32_t*>(sp2) = lo | (hi << 16);
-        } else {
-          *reinterpret_cast<float2*>(sp2) = make_float2(s2[0], s2[1]);
-        }
-      }
-    }
-  }
-
-  // one width for every head (the host launches it only for such states)
-  template <int BITS>
-  static __device__ void run_stream(const StepArgs& a) {
-    extern __shared__ float lds[];
-    const int tile = blockIdx.x;
-    const int bb = tile / a.H, h = tile - bb * a.H;
-    const HeadEntry he = head_entry(a, h);
-    uint8_t* tb = a.tiles + (size_t)bb * a.batch_stride + he.head_offset;
-    const int wrw = a.dk / WR;
-    const int nw = blockDim.x >> 6;
-    uint8_t* stg = reinterpret_cast<uint8_t*>(lds) + a.lds_stage + (threadIdx.x >> 6) * (512 * BITS);
-    Lds L{};
-    L.w = lds;
-    L.up = L.w + nw * WC;
-    L.op = L.up + 2 * wrw * a.dv;
-    uint32_t flags = 0;
-    body_stream<BITS>(a, he, tb, tile, L, flags, stg);
-    if (wrw > 1) {
-      __syncthreads();
-      BypassRegs br;
-      const PwPre pwp{};
-      combine_o(a, he, tb, tile, L, wrw, flags, false, br, pwp);
-    }
-    finish(a, tile, flags);
-  }
-
   // BOOST: every wavefront of the grid is resident from the start (the host
   // checks), and the ones still issuing their loads go ahead of those already
   // computing. With several rounds of workgroups this measured slower.
@@ -2054,41 +1605,6 @@ __global__ __launch_bounds__(512) void decode_kernel(StepArgs a) {
   Decode<MODEL, CL, FEAT, SPEC>::run(a);
 }
 
-// Rows without the delta rule, streamed one at a time (see run_stream), for
-// states whose heads share one width: at most 96 VGPRs, five wavefronts per
-// SIMD. Compile-time group size, scale mode and dtypes (SPEC); 4-bit codes
-// with 64-column groups are not streamed (that form needs more registers).
-template <int MODEL, int CL, int SPEC, int BITS>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(5))) void decode_stream_kernel(StepArgs a) {
-  Decode<MODEL, CL, kFeatPlain, SPEC>::template run_stream<BITS>(a);
-}
-
-template <int MODEL>
-DecodeFn decode_stream_pick(int cl, int spec, int bits) {
-  if constexpr (MODEL == kGDN) {
-    return nullptr;
-  } else {
-    if (cl == 4 && (spec == kSpecPersF16Bf16G32 || spec == kSpecDynF16Bf16G32)) {
-      const bool pers = spec == kSpecPersF16Bf16G32;
-      switch (bits) {
-        case 4: return pers ? decode_stream_kernel<MODEL, 4, kSpecPersF16Bf16G32, 4> : decode_stream_kernel<MODEL, 4, kSpecDynF16Bf16G32, 4>;
-        case 6: return pers ? decode_stream_kernel<MODEL, 4, kSpecPersF16Bf16G32, 6> : decode_stream_kernel<MODEL, 4, kSpecDynF16Bf16G32, 6>;
-        case 8: return pers ? decode_stream_kernel<MODEL, 4, kSpecPersF16Bf16G32, 8> : decode_stream_kernel<MODEL, 4, kSpecDynF16Bf16G32, 8>;
-        default: return nullptr;
-      }
-    }
-    if (cl == 8 && (spec == kSpecDynF32Bf16G64 || spec == kSpecDynF32F32G64)) {
-      const bool bfin = spec == kSpecDynF32Bf16G64;
-      switch (bits) {
-        case 6: return bfin ? decode_stream_kernel<MODEL, 8, kSpecDynF32Bf16G64, 6> : decode_stream_kernel<MODEL, 8, kSpecDynF32F32G64, 6>;
-        case 8: return bfin ? decode_stream_kernel<MODEL, 8, kSpecDynF32Bf16G64, 8> : decode_stream_kernel<MODEL, 8, kSpecDynF32F32G64, 8>;
-        default: return nullptr;
-      }
-    }
-    return nullptr;
-  }
-}
-
 // specialised steps held to at most 128 VGPRs: four wavefronts per SIMD
 template <int MODEL, int CL, int FEAT, int SPEC, bool BOOST = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel_occ(StepArgs a) {
@@ -2167,8 +1683,5 @@ DecodeFn decode_retnet(int cl, int feat, int spec);
 DecodeFn decode_mamba2(int cl, int feat, int spec);
 DecodeFn decode_gla(int cl, int feat, int spec);
 DecodeFn decode_gdn(int cl, int feat, int spec);
-DecodeFn decode_stream_retnet(int cl, int spec, int bits);
-DecodeFn decode_stream_mamba2(int cl, int spec, int bits);
-DecodeFn decode_stream_gla(int cl, int spec, int bits);
 
 }  // namespace rsq

@@ -3,5 +3,4 @@
 
 namespace rsq {
 DecodeFn decode_mamba2(int cl, int feat, int spec) { return decode_pick_cl<kMamba2>(cl, feat, spec); }
-DecodeFn decode_stream_mamba2(int cl, int spec, int bits) { return decode_stream_pick<kMamba2>(cl, spec, bits); }
 }  // namespace rsq

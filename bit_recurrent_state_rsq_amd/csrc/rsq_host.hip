@@ -567,13 +567,7 @@ rsq_status decode_step(rsq_state* st, const void* q, const void* k, const void* 
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && bf16 && g == 64) spec = 2;
   else if (sm == RSQ_SCALE_DYNAMIC && sf16 && bf16 && g == 32) spec = 3;
   else if (sm == RSQ_SCALE_DYNAMIC && !sf16 && !bf16 && g == 64) spec = 4;
-  // plain states whose heads share one width take the streamed-row step
-  // where it exists (same arithmetic, fewer registers)
-  // (same arithmetic, fewer registers)
-  rsq::DecodeFn fn = nullptr;
-  if (feat == rsq::kFeatPlain && st->uniform && spec != 0)
-    fn = rsq::decode_stream_for(model, st->geo.cl, spec, st->heads[0].bits);
-  if (!fn) fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
+  rsq::DecodeFn fn = rsq::decode_kernel_for(model, st->geo.cl, feat, spec);
   // quantized states without a bypass: every wavefront stages its code
   // chunks in LDS (512 bytes per code bit), after the step's own areas
   size_t lds = 0;

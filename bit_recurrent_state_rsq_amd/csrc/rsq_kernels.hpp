@@ -68,9 +68,6 @@ __device__ __forceinline__ HeadEntry head_entry(const StepArgs& a, int h) {
 
 typedef void (*DecodeFn)(StepArgs);
 DecodeFn decode_kernel_for(int model, int cl, int feat, int spec);
-// the streamed-row step of a plain state whose heads share one width, or
-// nullptr where that form does not apply (the delta rule, run-time flags)
-DecodeFn decode_stream_for(int model, int cl, int spec, int bits);
 // the raised-priority twin of a decode kernel for grids resident at once, or nullptr
 DecodeFn decode_boost_twin(DecodeFn fn);
 DecodeFn readout_kernel_for(int cl);

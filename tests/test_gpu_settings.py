@@ -1,15 +1,12 @@
 """GPU parity of the decode step's less common settings, against the CPU oracle.
 
-Plain states of the rows without the delta rule (RetNet, Mamba2, GLA) whose
-heads share one width run the streamed-row step when their group size, scale
-mode and dtypes have a compile-time form (group 32 with binary16 steps and
-bf16 inputs, group 64 with fp32 steps and bf16 or fp32 inputs). These cases
-cover the forms the workload-shaped tests do not reach: RetNet's gamma rows,
-fp32 inputs, 6- and 8-bit codes with 32-column groups, and a persistent
-trigger above 1, under which codes can leave the range and are clipped (for
-the Gated DeltaNet step too). Every step is checked: codes and step sizes
-bit-exact outside the 1e-6 decision windows, o_t within rel-L2 1e-4, the same
-teacher-forced protocol as the other parity tests.
+The workload-shaped tests leave some forms of the staged decode step
+unreached: RetNet's gamma rows with bf16 inputs, fp32 inputs with fp32 steps,
+6- and 8-bit codes with 32-column groups, and a persistent trigger above 1,
+under which codes can leave the range and are clipped (the only case where
+the clamp runs with normal steps). Every step is checked: codes and step
+sizes bit-exact outside the 1e-6 decision windows, o_t within rel-L2 1e-4,
+the same teacher-forced protocol as the other parity tests.
 """
 import pytest
 
